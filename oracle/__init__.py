@@ -1,0 +1,246 @@
+"""CPU oracle of the BitNet b1.58 BitLinear forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package. The HIP product path (``ternary_quantized_linear_amd``)
+neither imports it nor shares any code with it.
+
+The arithmetic lives in ``bitlinear_oracle.c`` (plain C loops, built with gcc
+``-O2 -ffp-contract=off -fno-fast-math -fopenmp``); this module compiles it on demand
+and wraps it with numpy arrays in and out. The header of the C file states, for each
+step, the passage of the pages it follows and the precision of every rounding:
+
+  1. gamma = exact sum |W| / (N*K) in fp64, beta = fp32(gamma)
+  2. codes = clamp(round_half_even(w * fp32(1/beta)), -1, 1)
+  3. four 2-bit codes per byte, u = q + 1, code k = 4j+i in bits [2i+1:2i] of byte j
+  4. RMSNorm: r = 1/sqrt(exact sum x^2 / K + eps) in fp64, y = fp32(x * r * g)
+  5. s_t = 127 / max(max|y|, 1e-5) in fp32, Xq = clamp(rint(y * s_t), -128, 127)
+  6. acc = Xq . codes^T in integers
+  7. Y = fp32(acc * beta / s_t) computed in fp64
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(brute force in exact rationals, library routines, closed forms, invariants and the
+worked examples under ``tests/golden/``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bitlinear_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+NO_NORM = 0x1
+
+_ERRORS = {
+    -1: "non-finite input",
+    -2: "bad dimensions",
+    -3: "out of memory",
+    -4: "invalid packed code (0b11) or code outside {-1,0,1}",
+    -5: "accumulator outside int32",
+}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc into oracle/liboracle.so."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-fopenmp", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            sig = {
+                "orc_set_threads": [ctypes.c_int],
+                "orc_abs_sum": [P, I64, P],
+                "orc_sum_sq": [P, I64, P],
+                "orc_weight_scale": [P, I64, I64, P, P],
+                "orc_ternarize": [P, I64, ctypes.c_float, P],
+                "orc_pack": [P, I64, I64, P],
+                "orc_unpack": [P, I64, I64, P],
+                "orc_quantize_weights": [P, I64, I64, P, P, P],
+                "orc_rmsnorm": [P, P, I64, I64, ctypes.c_float, P],
+                "orc_absmax_quant": [P, I64, I64, P, P],
+                "orc_quantize_acts": [P, P, I64, I64, ctypes.c_float, ctypes.c_uint32, P, P],
+                "orc_product": [P, P, I64, I64, I64, P],
+                "orc_rescale": [P, P, ctypes.c_float, I64, I64, P],
+                "orc_forward": [P, P, I64, I64, P, ctypes.c_float, I64, P, P],
+            }
+            for name, args in sig.items():
+                f = getattr(lib, name)
+                f.argtypes = args
+                f.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(st):
+    if st != 0:
+        raise OracleError(_ERRORS.get(st, "oracle error %d" % st))
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def set_threads(n: int = 0) -> int:
+    """Set the OpenMP thread count (0 keeps it); returns the count in effect."""
+    return _load().orc_set_threads(int(n))
+
+
+def abs_sum(w) -> float:
+    """Exact sum of |w| rounded once to fp64."""
+    w = _f32(w)
+    out = ctypes.c_double()
+    _check(_load().orc_abs_sum(_ptr(w), w.size, ctypes.addressof(out)))
+    return out.value
+
+
+def sum_sq(x) -> float:
+    """Exact sum of x^2 rounded once to fp64."""
+    x = _f32(x)
+    out = ctypes.c_double()
+    _check(_load().orc_sum_sq(_ptr(x), x.size, ctypes.addressof(out)))
+    return out.value
+
+
+def weight_scale(W):
+    """Returns (gamma64, beta32) of W [N, K]."""
+    W = _f32(W)
+    N, K = W.shape
+    g = ctypes.c_double()
+    b = ctypes.c_float()
+    _check(_load().orc_weight_scale(_ptr(W), N, K, ctypes.addressof(g), ctypes.addressof(b)))
+    return g.value, np.float32(b.value)
+
+
+def ternarize(W, beta):
+    W = _f32(W)
+    q = np.empty(W.shape, dtype=np.int8)
+    _check(_load().orc_ternarize(_ptr(W), W.size, float(np.float32(beta)), _ptr(q)))
+    return q
+
+
+def pack(q):
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    N, K = q.shape
+    P = np.empty((N, K // 4), dtype=np.uint8)
+    _check(_load().orc_pack(_ptr(q), N, K, _ptr(P)))
+    return P
+
+
+def unpack(P, K):
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    N = P.shape[0]
+    q = np.empty((N, K), dtype=np.int8)
+    _check(_load().orc_unpack(_ptr(P), N, K, _ptr(q)))
+    return q
+
+
+def quantize_weights(W):
+    """W [N, K] fp32 -> (packed uint8 [N, K/4], beta fp32, gamma fp64)."""
+    W = _f32(W)
+    N, K = W.shape
+    P = np.empty((N, K // 4), dtype=np.uint8)
+    b = ctypes.c_float()
+    g = ctypes.c_double()
+    _check(_load().orc_quantize_weights(_ptr(W), N, K, _ptr(P), ctypes.addressof(b),
+                                        ctypes.addressof(g)))
+    return P, np.float32(b.value), g.value
+
+
+def rmsnorm(X, gain=None, eps=1e-6):
+    X = _f32(X)
+    T, K = X.shape
+    g = None if gain is None else _f32(gain)
+    Y = np.empty_like(X)
+    _check(_load().orc_rmsnorm(_ptr(X), _ptr(g), T, K, float(np.float32(eps)), _ptr(Y)))
+    return Y
+
+
+def absmax_quant(Y):
+    Y = _f32(Y)
+    T, K = Y.shape
+    q = np.empty((T, K), dtype=np.int8)
+    s = np.empty(T, dtype=np.float32)
+    _check(_load().orc_absmax_quant(_ptr(Y), T, K, _ptr(q), _ptr(s)))
+    return q, s
+
+
+def quantize_acts(X, gain=None, eps=1e-6, flags=0):
+    """X [T, K] fp32 -> (Xq int8 [T, K], x_scale fp32 [T])."""
+    X = _f32(X)
+    T, K = X.shape
+    g = None if gain is None else _f32(gain)
+    q = np.empty((T, K), dtype=np.int8)
+    s = np.empty(T, dtype=np.float32)
+    _check(_load().orc_quantize_acts(_ptr(X), _ptr(g), T, K, float(np.float32(eps)),
+                                     int(flags), _ptr(q), _ptr(s)))
+    return q, s
+
+
+def product(Xq, P, K):
+    Xq = np.ascontiguousarray(Xq, dtype=np.int8)
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    T = Xq.shape[0]
+    N = P.shape[0]
+    acc = np.empty((T, N), dtype=np.int32)
+    _check(_load().orc_product(_ptr(Xq), _ptr(P), T, N, K, _ptr(acc)))
+    return acc
+
+
+def rescale(acc, s, beta):
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s = _f32(s)
+    T, N = acc.shape
+    Y = np.empty((T, N), dtype=np.float32)
+    _check(_load().orc_rescale(_ptr(acc), _ptr(s), float(np.float32(beta)), T, N, _ptr(Y)))
+    return Y
+
+
+def forward(Xq, s, P, beta):
+    """(Xq [T,K], s [T], packed [N,K/4], beta) -> (Y fp32 [T,N], acc int32 [T,N])."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.int8)
+    s = _f32(s)
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    T, K = Xq.shape
+    N = P.shape[0]
+    Y = np.empty((T, N), dtype=np.float32)
+    acc = np.empty((T, N), dtype=np.int32)
+    _check(_load().orc_forward(_ptr(Xq), _ptr(s), T, K, _ptr(P), float(np.float32(beta)), N,
+                               _ptr(Y), _ptr(acc)))
+    return Y, acc
+
+
+def bitlinear(X, W, gain=None, eps=1e-6, flags=0):
+    """The whole forward from fp32 X [T,K] and fp32 W [N,K]; returns a dict of stages."""
+    P, beta, gamma = quantize_weights(W)
+    Xq, s = quantize_acts(X, gain, eps, flags)
+    Y, acc = forward(Xq, s, P, beta)
+    return {"packed": P, "beta": beta, "gamma": gamma, "Xq": Xq, "x_scale": s,
+            "acc": acc, "Y": Y}

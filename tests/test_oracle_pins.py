@@ -1,0 +1,376 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks the oracle against exact-rational or 60-digit brute force, a library
+routine (math.fsum, a float64 BLAS matmul), a closed form, an invariant that the
+definitions fix, or a hand-worked fixture under tests/golden/. The tests are chosen
+so that a plausible slip in the oracle -- a wrong rounding mode, a per-row instead of
+a per-tensor scale, a sum instead of a mean, a misplaced epsilon, 128 in place of 127,
+a transposed operand, a flipped code sign, an inverted rescale -- fails at least one.
+"""
+import math
+import os
+import sys
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from golden.load import load  # noqa: E402
+
+F32 = np.float32
+
+
+def ulp32(x):
+    x = abs(float(x))
+    if x < 2.0 ** -126:
+        return 2.0 ** -149
+    return 2.0 ** (math.floor(math.log2(x)) - 23)
+
+
+# ---------------------------------------------------------------- exact sums (gamma)
+
+def _fraction_abs_sum(a):
+    return sum((Fraction(float(v)) for v in np.abs(a.astype(np.float64)).ravel()), Fraction(0))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_abs_sum_equals_exact_rational(seed):
+    # values over ~250 binades, denormals included: naive float sums lose them
+    a = workloads.wide_range(2000, seed)
+    exact = _fraction_abs_sum(a)
+    assert oracle.abs_sum(a) == float(exact)  # float(Fraction) rounds correctly
+
+
+def test_abs_sum_equals_math_fsum_large():
+    r = np.random.default_rng(7)
+    a = (r.standard_normal(3_000_000) * np.exp(r.uniform(-30, 30, 3_000_000))).astype(np.float32)
+    assert oracle.abs_sum(a) == math.fsum(np.abs(a.astype(np.float64)).tolist())
+
+
+def test_abs_sum_rounding_ties():
+    # 1 + 2^-53 is a midpoint between 1 and 1 + 2^-52: ties to even gives 1;
+    # a further 2^-80 puts the exact sum above the midpoint: the result must round up.
+    assert oracle.abs_sum(np.array([1.0, 2.0 ** -53], np.float32)) == 1.0
+    assert oracle.abs_sum(np.array([1.0, 2.0 ** -53, 2.0 ** -80], np.float32)) == 1.0 + 2.0 ** -52
+    assert oracle.abs_sum(np.array([2.0 ** -80, 2.0 ** -53, 1.0], np.float32)) == 1.0 + 2.0 ** -52
+    # 2^-110 lies more than 53 binades below 2^-53, so no two parts can merge: the sum
+    # is held as 1 + 2^-53 (an exact midpoint) plus 2^-110, and must still round up
+    assert oracle.abs_sum(np.array([1.0, 2.0 ** -53, 2.0 ** -110], np.float32)) == 1.0 + 2.0 ** -52
+    # 1 + 3*2^-53 is a midpoint between 1+2^-52 and 1+2^-51: even is 1+2^-51
+    v = np.array([1.0, 2.0 ** -52, 2.0 ** -53], np.float32)
+    assert oracle.abs_sum(v) == 1.0 + 2.0 ** -51
+
+
+def test_abs_sum_order_and_thread_independent():
+    a = workloads.weights(512, 4096, 3).ravel()
+    perm = np.random.default_rng(1).permutation(a.size)
+    oracle.set_threads(1)
+    one = oracle.abs_sum(a)
+    oracle.set_threads(os.cpu_count() or 1)
+    assert oracle.abs_sum(a[perm]) == one
+    assert oracle.abs_sum(a[::-1].copy()) == one
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_sum_sq_equals_exact_rational(seed):
+    a = workloads.wide_range(1000, seed, lo_exp=-60, hi_exp=60)
+    exact = sum((Fraction(float(v)) ** 2 for v in a.astype(np.float64)), Fraction(0))
+    assert oracle.sum_sq(a) == float(exact)
+
+
+def test_oracle_rejects_nonfinite():
+    for bad in (np.inf, -np.inf, np.nan):
+        with pytest.raises(oracle.OracleError):
+            oracle.abs_sum(np.array([1.0, bad], np.float32))
+        with pytest.raises(oracle.OracleError):
+            oracle.quantize_acts(np.array([[1.0, bad, 0.0, 0.0]], np.float32))
+
+
+# ---------------------------------------------------------------- weight scale / codes
+
+@pytest.mark.parametrize("shape", [(3, 8), (7, 12), (16, 64)])
+def test_weight_scale_equals_exact_rational(shape):
+    N, K = shape
+    W = workloads.wide_range(N * K, N, lo_exp=-40, hi_exp=5).reshape(N, K)
+    gamma, beta = oracle.weight_scale(W)
+    S = float(_fraction_abs_sum(W))          # exact sum, one rounding to fp64
+    g = S / float(N * K)                     # fp64 division
+    assert gamma == g
+    assert beta == F32(g)
+
+
+def test_weight_scale_is_mean_over_gaussian():
+    # closed form: E|w| = sigma * sqrt(2/pi) for w ~ N(0, sigma^2)
+    W = workloads.weights(1024, 4096, 11)
+    gamma, _ = oracle.weight_scale(W)
+    n = W.size
+    ratio = gamma / workloads.WEIGHT_SIGMA
+    se = math.sqrt(1 - 2 / math.pi) / math.sqrt(n)  # std error of mean|z|
+    assert abs(ratio - math.sqrt(2 / math.pi)) < 5 * se
+
+
+def test_weight_scale_power_of_two_equivariance():
+    W = workloads.weights(64, 256, 2)
+    g0, b0 = oracle.weight_scale(W)
+    for k in (-7, 3, 20):
+        gk, bk = oracle.weight_scale((W * F32(2.0 ** k)).astype(np.float32))
+        assert gk == g0 * 2.0 ** k and bk == b0 * F32(2.0 ** k)
+
+
+def test_golden_weights_ties():
+    g = load("weights_ties.txt")
+    W = np.array(g["W"], np.float32)
+    P, beta, gamma = oracle.quantize_weights(W)
+    assert gamma == g["gamma"] and beta == g["beta"]
+    q = oracle.ternarize(W, beta)
+    assert q.tolist() == g["codes"]
+    assert P.tolist() == g["packed"]
+
+
+def test_golden_per_tensor_scale():
+    g = load("weights_per_tensor.txt")
+    W = np.array(g["W"], np.float32)
+    P, beta, gamma = oracle.quantize_weights(W)
+    assert gamma == g["gamma"]
+    assert oracle.unpack(P, W.shape[1]).tolist() == g["codes"]
+
+
+def test_codes_invariants_and_gaussian_zero_fraction():
+    # closed form: q = 0 iff |w| <= gamma/2 with gamma = sigma*sqrt(2/pi), so the
+    # zero fraction is 2*Phi(sqrt(2/pi)/2) - 1 = 0.31006 and each sign 0.34497.
+    W = workloads.weights(1024, 2048, 5)
+    P, beta, _ = oracle.quantize_weights(W)
+    q = oracle.unpack(P, 2048)
+    assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+    z = math.sqrt(2 / math.pi) / 2
+    p0 = math.erf(z / math.sqrt(2))
+    frac0 = float(np.mean(q == 0))
+    assert abs(p0 - 0.31006) < 1e-4
+    assert abs(frac0 - p0) < 0.002
+    assert abs(float(np.mean(q == 1)) - (1 - p0) / 2) < 0.002
+    assert abs(float(np.mean(q == -1)) - (1 - p0) / 2) < 0.002
+    # the sign of every non-zero code is the sign of its weight
+    nz = q != 0
+    assert np.all(np.sign(W[nz]) == q[nz])
+
+
+def test_codes_special_cases():
+    # constant matrix: scale 1/c maps every weight to exactly 1
+    W = np.full((4, 8), 0.37, np.float32)
+    P, beta, _ = oracle.quantize_weights(W)
+    assert beta == F32(0.37) and np.all(oracle.unpack(P, 8) == 1)
+    # all zero: beta = 0 and every code 0
+    P, beta, _ = oracle.quantize_weights(np.zeros((2, 4), np.float32))
+    assert beta == 0 and np.all(oracle.unpack(P, 4) == 0)
+    # denormal-only weights: beta below FLT_MIN gives all codes 0
+    W = np.full((2, 4), 1e-40, np.float32)
+    P, beta, _ = oracle.quantize_weights(W)
+    assert beta < np.finfo(np.float32).tiny and np.all(oracle.unpack(P, 4) == 0)
+    # one outlier dominates the mean: the others round to 0, the outlier clamps to 1
+    W = np.zeros((1, 8), np.float32)
+    W[0, 3] = -100.0
+    W[0, 5] = 0.01
+    P, beta, _ = oracle.quantize_weights(W)
+    assert oracle.unpack(P, 8).tolist() == [[0, 0, 0, -1, 0, 0, 0, 0]]
+
+
+# ---------------------------------------------------------------- packing
+
+def test_pack_roundtrip_and_layout():
+    r = np.random.default_rng(3)
+    q = r.integers(-1, 2, size=(37, 64)).astype(np.int8)
+    P = oracle.pack(q)
+    assert P.shape == (37, 16) and P.nbytes == 37 * 64 // 4
+    assert np.array_equal(oracle.unpack(P, 64), q)
+    # independent decode: code k = 4j+i sits in bits [2i+1:2i] of byte j, as q+1
+    dec = np.stack([((P >> (2 * i)) & 3).astype(np.int8) - 1 for i in range(4)], axis=-1)
+    assert np.array_equal(dec.reshape(37, 64), q)
+
+
+def test_unpack_rejects_unused_pattern():
+    with pytest.raises(oracle.OracleError):
+        oracle.unpack(np.array([[0b11000000]], np.uint8), 4)
+
+
+def test_pack_density_matches_page_counts():
+    g = load("page_counts.txt")
+    n_proj = sum(N * K for (N, K) in workloads.LLAMA3_8B.values()) * workloads.LLAMA3_8B_LAYERS
+    packed_elems = n_proj // 4             # four 2-bit codes per int8 element
+    assert n_proj == 6_979_321_856 and packed_elems == 1_744_830_464
+    # the rest of the 8B model (embeddings, head, norms) stays unpacked
+    rest = 8.03e9 - n_proj
+    assert abs((packed_elems + rest) - g["params_after"]) < 0.05e9
+    # 2 bits per weight is 87.5% below 16; the entropy figure log2(3) is the page's ~90%
+    assert abs(math.log2(3) - g["bits_ternary"]) < 0.005
+    assert abs((1 - g["bits_ternary"] / g["bits_fp16"]) - g["memory_saving_approx"]) < 0.01
+    assert 1 - 2 / 16 == 0.875
+
+
+# ---------------------------------------------------------------- activations
+
+def test_golden_acts_ties():
+    g = load("acts_ties.txt")
+    X = np.array(g["X"], np.float32)
+    q, s = oracle.quantize_acts(X, flags=oracle.NO_NORM)
+    assert q.tolist() == g["codes"] and s.tolist() == g["x_scale"]
+
+
+def _decimal_rmsnorm(x, eps, gain=None):
+    getcontext().prec = 60
+    d = [Decimal(float(v)) for v in x]
+    ms = sum(v * v for v in d) / len(d)
+    r = 1 / (ms + Decimal(float(F32(eps)))).sqrt()
+    if gain is None:
+        return [v * r for v in d]
+    return [v * r * Decimal(float(gv)) for v, gv in zip(d, gain)]
+
+
+@pytest.mark.parametrize("seed,gain", [(0, False), (1, True), (2, False)])
+def test_rmsnorm_and_codes_against_decimal(seed, gain):
+    K = 96
+    X = workloads.acts_student_t(3, K, seed)
+    X[1] *= F32(1e-3)  # a token whose mean square is near eps
+    g = (1 + 0.5 * np.random.default_rng(seed).standard_normal(K)).astype(np.float32) if gain else None
+    Y = oracle.rmsnorm(X, g, 1e-6)
+    q, s = oracle.quantize_acts(X, g, 1e-6)
+    for t in range(X.shape[0]):
+        ye = _decimal_rmsnorm(X[t], 1e-6, g)
+        for k in range(K):
+            err = abs(Decimal(float(Y[t, k])) - ye[k])
+            assert err <= Decimal(0.5000001) * Decimal(ulp32(float(ye[k])))
+        m = max(abs(float(v)) for v in Y[t])
+        se = Decimal(127) / Decimal(max(m, float(F32(1e-5))))
+        assert abs(Decimal(float(s[t])) - se) <= Decimal(0.5) * Decimal(ulp32(float(se)))
+        for k in range(K):
+            v = Decimal(float(Y[t, k])) * Decimal(float(s[t]))
+            frac = abs(v - v.to_integral_value(rounding="ROUND_FLOOR") - Decimal("0.5"))
+            if frac > Decimal("1e-4"):  # away from a tie, fp32 rounding cannot matter
+                assert int(q[t, k]) == int(v.to_integral_value(rounding="ROUND_HALF_EVEN"))
+
+
+def test_rmsnorm_mean_square_closed_form():
+    # mean(y^2) = ms / (ms + eps) before rounding: a token with ms = eps gives 1/2
+    r = np.random.default_rng(4)
+    x = r.standard_normal(4096)
+    x = x / np.sqrt(np.mean(x * x)) * 1e-3          # ms = 1e-6 = eps (up to rounding)
+    X = x.astype(np.float32)[None, :]
+    ms = float(np.mean(X.astype(np.float64) ** 2))
+    Y = oracle.rmsnorm(X, None, 1e-6).astype(np.float64)
+    expect = ms / (ms + float(F32(1e-6)))
+    assert abs(float(np.mean(Y * Y)) - expect) < 1e-6
+    assert abs(expect - 0.5) < 1e-3
+    # and a unit-scale token is normalized to mean square ~1
+    X = workloads.acts_normal(1, 4096, 9)
+    Y = oracle.rmsnorm(X, None, 1e-6).astype(np.float64)
+    assert abs(float(np.mean(Y * Y)) - 1.0) < 1e-5
+
+
+def test_act_codes_invariants():
+    X = np.concatenate([workloads.acts_normal(8, 1024, 1), workloads.acts_student_t(8, 1024, 2)])
+    q, s = oracle.quantize_acts(X)
+    assert q.min() >= -127 and q.max() <= 127          # -128 never appears with 127
+    assert np.all(np.abs(q.astype(np.int32)).max(axis=1) == 127)
+    Y = oracle.rmsnorm(X)
+    assert np.all(np.sign(q) == np.where(q == 0, 0, np.sign(Y)))
+
+
+def test_act_special_rows():
+    K = 64
+    X = np.zeros((4, K), np.float32)
+    X[0] = 0.3                    # constant row -> all +127
+    X[1, 5] = -2.0                # one-hot row -> one -127, the rest 0
+    X[3] = -1e3                   # constant negative row -> all -127
+    q, s = oracle.quantize_acts(X)
+    assert np.all(q[0] == 127) and np.all(q[3] == -127)
+    assert q[1, 5] == -127 and np.count_nonzero(q[1]) == 1
+    assert np.all(q[2] == 0) and s[2] == F32(127.0) / F32(1e-5)   # zero row: floor 1e-5
+
+
+def test_act_quant_scale_invariance_without_eps():
+    # with eps = 0, RMSNorm is invariant under x -> 2^k x, bit for bit
+    X = workloads.acts_normal(4, 512, 3)
+    q0, s0 = oracle.quantize_acts(X, eps=0.0)
+    for k in (-20, 5):
+        qk, sk = oracle.quantize_acts((X * F32(2.0 ** k)).astype(np.float32), eps=0.0)
+        assert np.array_equal(q0, qk) and np.array_equal(s0, sk)
+
+
+# ---------------------------------------------------------------- product and rescale
+
+def test_golden_forward():
+    gw, ga, gf = load("weights_ties.txt"), load("acts_ties.txt"), load("forward_small.txt")
+    out = oracle.bitlinear(np.array(ga["X"], np.float32), np.array(gw["W"], np.float32),
+                           flags=oracle.NO_NORM)
+    assert out["acc"].tolist() == gf["acc"]
+    assert out["Y"].tolist() == gf["Y"]
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 7, 16), (5, 33, 100), (16, 64, 1024)])
+def test_product_add_sub_and_blas(T, N, K):
+    r = np.random.default_rng(T * N + K)
+    Xq = r.integers(-127, 128, size=(T, K)).astype(np.int8)
+    q = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    acc = oracle.product(Xq, oracle.pack(q), K)
+    x = Xq.astype(np.int64)
+    # add/subtract form: only additions of +x and -x, no multiplications
+    addsub = np.stack([(x * (q[o] == 1)).sum(1) - (x * (q[o] == -1)).sum(1) for o in range(N)], 1)
+    assert np.array_equal(acc, addsub)
+    # a float64 BLAS matmul of the integer matrices is exact here (|acc| < 2^53)
+    assert np.array_equal(acc, (Xq.astype(np.float64) @ q.astype(np.float64).T).astype(np.int64))
+
+
+def test_product_python_int_bruteforce():
+    r = np.random.default_rng(0)
+    Xq = r.integers(-127, 128, size=(3, 12)).astype(np.int8)
+    q = r.integers(-1, 2, size=(5, 12)).astype(np.int8)
+    acc = oracle.product(Xq, oracle.pack(q), 12)
+    for t in range(3):
+        for o in range(5):
+            assert acc[t, o] == sum(int(Xq[t, k]) * int(q[o, k]) for k in range(12))
+
+
+def test_product_extreme_magnitude():
+    K = 28672
+    Xq = np.full((1, K), 127, np.int8)
+    q = np.ones((2, K), np.int8)
+    q[1] = -1
+    acc = oracle.product(Xq, oracle.pack(q), K)
+    assert acc.tolist() == [[127 * K, -127 * K]]
+
+
+def test_rescale_against_exact_rational():
+    r = np.random.default_rng(5)
+    acc = r.integers(-300000, 300000, size=(4, 50)).astype(np.int32)
+    acc[0, 0] = 0
+    s = (r.uniform(0.5, 200, 4)).astype(np.float32)
+    beta = F32(0.0159)
+    Y = oracle.rescale(acc, s, beta)
+    assert Y[0, 0] == 0.0
+    for t in range(4):
+        for o in range(50):
+            e = Fraction(int(acc[t, o])) * Fraction(float(beta)) / Fraction(float(s[t]))
+            assert abs(Fraction(float(Y[t, o])) - e) <= Fraction(0.5000001) * Fraction(ulp32(float(e)))
+
+
+def test_forward_equals_dequantized_matmul():
+    # y = (Xq / s) (beta * q)^T: dequantized activations times dequantized weights
+    W = workloads.weights(*workloads.TINY_W, seed=0)
+    X = workloads.acts_normal(workloads.TINY_T, workloads.TINY_W[1], seed=1)
+    out = oracle.bitlinear(X, W)
+    q = oracle.unpack(out["packed"], W.shape[1]).astype(np.float64)
+    xd = out["Xq"].astype(np.float64) / out["x_scale"].astype(np.float64)[:, None]
+    ref = xd @ (float(out["beta"]) * q).T
+    assert np.allclose(out["Y"], ref, rtol=1e-6, atol=1e-30)
+    # closed form of the agreement with the unquantized RMSNorm(X) W^T: for Gaussian w
+    # and q = sign(w) [|w| > c sigma], c = sqrt(2/pi)/2, corr(w, q) = 2 phi(c) / sqrt(P(|z| > c))
+    c = math.sqrt(2 / math.pi) / 2
+    phi = math.exp(-c * c / 2) / math.sqrt(2 * math.pi)
+    corr = 2 * phi / math.sqrt(1 - math.erf(c / math.sqrt(2)))
+    assert abs(corr - 0.8866) < 1e-3
+    full = oracle.rmsnorm(X).astype(np.float64) @ W.astype(np.float64).T
+    cos = np.sum(full * out["Y"]) / np.linalg.norm(full) / np.linalg.norm(out["Y"])
+    assert abs(cos - corr) < 0.01

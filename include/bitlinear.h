@@ -1,0 +1,199 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear.so: the BitNet b1.58 BitLinear forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (abbreviations used below):
+ *   [HF-1.58]    "Fine-tuning LLMs to 1.58 bits: extreme quantization with BitNet"
+ *                (summary of the Hugging Face post, agentlenshq.com)
+ *   [bitnet.cpp] "Microsoft's inference framework brings 1-bit large language models
+ *                to local devices" (unite.ai)
+ *   [b1.58]      "[Paper review] The Era of 1-bit LLMs: All Large Language Models are
+ *                in 1.58 Bits" (nubint.ai)
+ *
+ * The forward is split the way the pages split it: an offline weight conversion into
+ * packed 2-bit codes ([HF-1.58] "Key findings"; [bitnet.cpp] the i2_s conversion of
+ * "Build and prepare the project"), then per call "quantize the input, run the
+ * low-bit matrix product, multiply by the scale" ([bitnet.cpp] "CPU optimization",
+ * bitlinear_forward). Activation quantization is its own call so that projections
+ * that read the same input (q/k/v, gate/up) quantize it once.
+ *
+ * Conventions shared by every entry point:
+ *   - Shapes follow nn.Linear: W is [N out, K in] row-major (K contiguous), X is
+ *     [T tokens, K] row-major, Y = X W^T is [T, N] row-major.
+ *   - Every array pointer is a DEVICE pointer owned by the caller; the library keeps
+ *     no pointer after the stream-ordered work that uses it has finished, keeps no
+ *     device state, and allocates no device memory.
+ *   - Every compute call is asynchronous on `stream` (NULL = the default stream) and
+ *     performs no host synchronization; scales stay on the device.
+ *   - Arguments are validated on the host before anything is launched; an invalid call
+ *     returns its status without touching the GPU, so validation is testable without
+ *     one. BL_ERR_HIP reports a failed launch (text from bitlinear_last_hip_error()).
+ *   - Data-dependent conditions are not reported: with NaN or Inf inputs the values
+ *     written are unspecified, but every kernel still terminates.
+ *   - Array base pointers must be 16-byte aligned (BL_ERR_ALIGN otherwise).
+ *   - Calls on distinct streams with distinct output buffers may run concurrently.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* bl_stream_t; /* the same handle type as hipStream_t */
+
+typedef enum bl_status {
+  BL_OK = 0,
+  BL_ERR_NULL = 1,         /* a required pointer is NULL */
+  BL_ERR_DIM = 2,          /* T, N or K <= 0, or K not a multiple of 4 */
+  BL_ERR_K_TOO_LARGE = 3,  /* K > BL_MAX_K */
+  BL_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than its query returned */
+  BL_ERR_ALIGN = 5,        /* an array base pointer is not 16-byte aligned */
+  BL_ERR_HIP = 6,          /* a HIP call failed */
+  BL_ERR_ARG = 7           /* another invalid argument (flags, eps, count, kernel) */
+} bl_status;
+
+/* Largest K: |acc| <= 127*K must stay below 2^24 so that the int32 accumulator
+ * converts to fp32 exactly in the rescale (127 * 132104 = 16,777,208 < 2^24). */
+#define BL_MAX_K 132104
+/* Largest number of entries in one grouped call. */
+#define BL_MAX_GROUP 8
+/* bitlinear_quantize_acts flag: skip RMSNorm and quantize X itself (y = x). */
+#define BL_NO_NORM 0x1u
+#define BL_ABI_VERSION 1
+
+/* Kernel selection for bitlinear_forward_ex (BL_KERNEL_AUTO is what
+ * bitlinear_forward uses). */
+typedef enum bl_kernel {
+  BL_KERNEL_AUTO = 0,
+  BL_KERNEL_GEMV = 1,     /* decode GEMV, int8 dot4; needs T <= 2 and K % 64 == 0 */
+  BL_KERNEL_SKINNY = 2,   /* skinny int8 MFMA GEMM; needs T <= 64 and K % 256 == 0 */
+  BL_KERNEL_PREFILL = 3,  /* LDS-tiled int8 MFMA GEMM; needs K % 128 == 0 */
+  BL_KERNEL_GENERIC = 4   /* any K % 4 == 0, any T: one thread per output */
+} bl_kernel;
+
+/* ---------------------------------------------------------------- weights
+ *
+ * Absmean ternary quantization and 2-bit packing ([HF-1.58] "How quantization
+ * works", weights: per-tensor scale = reciprocal of the mean absolute value, then
+ * scale, round, clamp to [-1, 1]; [b1.58] "Proposed method", absmean; packing four
+ * codes per int8, [HF-1.58] "Key findings"). Computes, exactly as specified:
+ *   S      = sum of |W| over all N*K entries, exact, rounded once to fp64
+ *   gamma  = S / (N*K) in fp64;  beta = fp32(gamma) (round to nearest even)
+ *   q      = clamp(rint(w * fp32(1/beta)), -1, 1), w * (1/beta) one fp32 product,
+ *            rint rounding half to even; all codes 0 when beta < FLT_MIN
+ *   packed = byte j of row o holds code k = 4j+i in bits [2i+1:2i] as u = q+1 (0..2)
+ * Arguments:
+ *   W          device fp32 [N, K], 16-byte aligned; read only
+ *   W_packed   device uint8 [N, K/4]; written
+ *   w_scale    device fp32 [1]; receives beta
+ *   w_gamma    device fp64 [1] or NULL; receives gamma
+ *   workspace  device scratch of at least bitlinear_weight_workspace_bytes(N, K)
+ *              bytes, 16-byte aligned; contents on entry are ignored
+ * The result is independent of launch order and bit-for-bit reproducible. */
+size_t bitlinear_weight_workspace_bytes(int64_t N, int64_t K);
+bl_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
+                                     uint8_t* W_packed, float* w_scale, double* w_gamma,
+                                     void* workspace, size_t workspace_bytes,
+                                     bl_stream_t stream);
+
+/* ---------------------------------------------------------------- activations
+ *
+ * Fused RMSNorm + per-token absmax int8 quantization ([b1.58] "Proposed method",
+ * RMSNorm; [HF-1.58] "How quantization works", activations: a norm before the
+ * quantizer, absmax per token into [-128, 127]; [bitnet.cpp] "2. Activation
+ * quantization", gamma = ||x||_inf and an epsilon). Per token t:
+ *   ss  = sum_k x_k^2 in fp64 (each square exact; double-double accumulation,
+ *         rounded once)
+ *   r   = 1 / sqrt(ss / K + eps) in fp64 (IEEE division and square root)
+ *   y_k = fp32((x_k * r) * g_k), both products in fp64 (no g product when gain is NULL)
+ *   s_t = 127 / max(max_k |y_k|, 1e-5) in fp32
+ *   Xq  = clamp(rint(y_k * s_t), -128, 127), y_k * s_t one fp32 product
+ * With BL_NO_NORM in flags, y = x (gain and eps are ignored).
+ * Arguments:
+ *   X        device fp32 [T, K], 16-byte aligned
+ *   gain     device fp32 [K] or NULL (unit gain)
+ *   eps      finite, >= 0 (1e-6 in the Llama-shaped workloads)
+ *   Xq       device int8 [T, K]; written
+ *   x_scale  device fp32 [T]; receives s_t */
+bl_status bitlinear_quantize_acts(const float* X, const float* gain, int64_t T, int64_t K,
+                                  float eps, uint32_t flags, int8_t* Xq, float* x_scale,
+                                  bl_stream_t stream);
+
+/* One entry of a grouped activation quantization: all entries share T, eps, flags. */
+typedef struct bl_act_desc {
+  const float* X;     /* device fp32 [T, K] */
+  const float* gain;  /* device fp32 [K] or NULL */
+  int8_t* Xq;         /* device int8 [T, K] */
+  float* x_scale;     /* device fp32 [T] */
+  int64_t K;
+} bl_act_desc;
+
+/* bitlinear_quantize_acts over `count` (1..BL_MAX_GROUP) independent inputs in one
+ * launch; each entry computes exactly what bitlinear_quantize_acts computes. */
+bl_status bitlinear_quantize_acts_grouped(const bl_act_desc* descs, int count, int64_t T,
+                                          float eps, uint32_t flags, bl_stream_t stream);
+
+/* ---------------------------------------------------------------- forward
+ *
+ * Ternary x int8 product with exact integer accumulation and the rescale
+ * ([HF-1.58] "Computation paradigm": integer additions in place of multiply-adds;
+ * "Inference optimization and custom kernels": weights unpacked on the fly inside
+ * the product; [bitnet.cpp] "3. BitLinear operation": multiply by the weight scale
+ * and the activation dequantization factor; no bias, [b1.58] "Proposed method"):
+ *   acc[t, o] = sum_k Xq[t, k] * q[o, k]        (exact, int32)
+ *   Y[t, o]   = fp32(acc) * fp32(beta / s_t)    (fp32; within 2 roundings of the
+ *                                                exact acc * beta / s_t)
+ * Arguments:
+ *   Xq, x_scale  outputs of bitlinear_quantize_acts: int8 [T, K], fp32 [T]
+ *   W_packed     uint8 [N, K/4] from bitlinear_quantize_weights; w_scale fp32 [1]
+ *   Y            device fp32 [T, N]; written
+ *   acc          device int32 [T, N] or NULL; receives the exact accumulators
+ * K <= BL_MAX_K. Byte patterns 0b11 in W_packed are outside the format; their
+ * contribution is unspecified. */
+bl_status bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                            const uint8_t* W_packed, const float* w_scale, int64_t N,
+                            float* Y, int32_t* acc, bl_stream_t stream);
+
+/* bitlinear_forward with an explicit kernel choice (for tests and measurement).
+ * Returns BL_ERR_ARG when the chosen kernel does not support the shape. */
+bl_status bitlinear_forward_ex(const int8_t* Xq, const float* x_scale, int64_t T,
+                               int64_t K, const uint8_t* W_packed, const float* w_scale,
+                               int64_t N, float* Y, int32_t* acc, bl_kernel kernel,
+                               bl_stream_t stream);
+
+/* The kernel bitlinear_forward would run for this shape. */
+bl_kernel bitlinear_forward_choice(int64_t T, int64_t N, int64_t K);
+
+/* One projection of a grouped forward: all entries share T. */
+typedef struct bl_proj_desc {
+  const int8_t* Xq;         /* int8 [T, K] */
+  const float* x_scale;     /* fp32 [T] */
+  const uint8_t* W_packed;  /* uint8 [N, K/4] */
+  const float* w_scale;     /* fp32 [1] */
+  float* Y;                 /* fp32 [T, N] */
+  int32_t* acc;             /* int32 [T, N] or NULL */
+  int64_t N;
+  int64_t K;
+} bl_proj_desc;
+
+/* bitlinear_forward over `count` (1..BL_MAX_GROUP) projections, each with its own
+ * weights, scale, input and output (for example q/k/v, or the seven projections of a
+ * decoder layer), in as few launches as the shapes allow (one per distinct K on the
+ * decode path). Each entry's results are those of bitlinear_forward. */
+bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_t T,
+                                    bl_stream_t stream);
+
+/* ---------------------------------------------------------------- misc */
+const char* bitlinear_status_str(bl_status s);
+/* Text of the last failing HIP call made by this thread ("" if none). */
+const char* bitlinear_last_hip_error(void);
+int bitlinear_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

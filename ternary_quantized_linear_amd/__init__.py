@@ -1,0 +1,229 @@
+"""Python binding of libbitlinear.so, the BitNet b1.58 BitLinear forward on MI355X.
+
+Argument marshalling only: every step runs in the library's HIP kernels. torch
+provides device memory and the current stream; no computation happens here. The
+functions named ``bitlinear_*`` mirror the C ABI of include/bitlinear.h one to one
+(tensors in place of pointers); ``quantize_weights``, ``quantize_acts``, ``forward``
+and ``BitLinear`` allocate their outputs and call them.
+
+If the shared library is missing, importing this package raises ImportError: there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BitLinearError", "lib_path", "bitlinear_weight_workspace_bytes",
+    "bitlinear_quantize_weights", "bitlinear_quantize_acts",
+    "bitlinear_quantize_acts_grouped", "bitlinear_forward", "bitlinear_forward_ex",
+    "bitlinear_forward_choice", "bitlinear_forward_grouped", "bitlinear_status_str",
+    "bitlinear_last_hip_error", "bitlinear_abi_version", "quantize_weights",
+    "quantize_acts", "forward", "BitLinear", "KERNELS", "NO_NORM", "MAX_K", "MAX_GROUP",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libbitlinear.so")
+
+NO_NORM = 0x1
+MAX_K = 132104
+MAX_GROUP = 8
+ABI_VERSION = 1
+KERNELS = {"auto": 0, "gemv": 1, "skinny": 2, "prefill": 3, "generic": 4}
+_KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        "libbitlinear.so is not built (%s); run ternary_quantized_linear_amd/build.py or "
+        "__graft_entry__.build()" % lib_path)
+
+_lib = ctypes.CDLL(lib_path)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+class _ActDesc(ctypes.Structure):
+    _fields_ = [("X", _P), ("gain", _P), ("Xq", _P), ("x_scale", _P), ("K", _I64)]
+
+
+class _ProjDesc(ctypes.Structure):
+    _fields_ = [("Xq", _P), ("x_scale", _P), ("W_packed", _P), ("w_scale", _P),
+                ("Y", _P), ("acc", _P), ("N", _I64), ("K", _I64)]
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_c_ws_bytes = _sig("bitlinear_weight_workspace_bytes", [_I64, _I64], ctypes.c_size_t)
+_c_qw = _sig("bitlinear_quantize_weights", [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P])
+_c_qa = _sig("bitlinear_quantize_acts",
+             [_P, _P, _I64, _I64, ctypes.c_float, ctypes.c_uint32, _P, _P, _P])
+_c_qag = _sig("bitlinear_quantize_acts_grouped",
+              [ctypes.POINTER(_ActDesc), ctypes.c_int, _I64, ctypes.c_float, ctypes.c_uint32, _P])
+_c_fw = _sig("bitlinear_forward", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P])
+_c_fwx = _sig("bitlinear_forward_ex",
+              [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_int, _P])
+_c_choice = _sig("bitlinear_forward_choice", [_I64, _I64, _I64])
+_c_fwg = _sig("bitlinear_forward_grouped", [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
+_c_str = _sig("bitlinear_status_str", [ctypes.c_int], ctypes.c_char_p)
+_c_err = _sig("bitlinear_last_hip_error", [], ctypes.c_char_p)
+_c_ver = _sig("bitlinear_abi_version", [])
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = "%s: %s" % (where, _c_str(status).decode())
+        if status == 6:
+            msg += " (%s)" % _c_err().decode()
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status, where):
+    if status != 0:
+        raise BitLinearError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+# ---------------------------------------------------------------- C ABI mirror
+
+def bitlinear_status_str(status: int) -> str:
+    return _c_str(status).decode()
+
+
+def bitlinear_last_hip_error() -> str:
+    return _c_err().decode()
+
+
+def bitlinear_abi_version() -> int:
+    return _c_ver()
+
+
+def bitlinear_weight_workspace_bytes(N: int, K: int) -> int:
+    return int(_c_ws_bytes(N, K))
+
+
+def bitlinear_quantize_weights(W, W_packed, w_scale, w_gamma, workspace, stream=None):
+    N, K = W.shape
+    _check(_c_qw(_ptr(W), N, K, _ptr(W_packed), _ptr(w_scale), _ptr(w_gamma), _ptr(workspace),
+                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                 _stream(W, stream)), "bitlinear_quantize_weights")
+
+
+def bitlinear_quantize_acts(X, gain, eps, flags, Xq, x_scale, stream=None):
+    T, K = X.shape
+    _check(_c_qa(_ptr(X), _ptr(gain), T, K, float(eps), int(flags), _ptr(Xq), _ptr(x_scale),
+                 _stream(X, stream)), "bitlinear_quantize_acts")
+
+
+def bitlinear_quantize_acts_grouped(entries, T, eps, flags, stream=None):
+    """entries: list of (X, gain, Xq, x_scale)."""
+    arr = (_ActDesc * len(entries))()
+    for i, (X, gain, Xq, xs) in enumerate(entries):
+        arr[i] = _ActDesc(X.data_ptr(), None if gain is None else gain.data_ptr(), Xq.data_ptr(),
+                          xs.data_ptr(), X.shape[-1])
+    _check(_c_qag(arr, len(entries), T, float(eps), int(flags), _stream(entries[0][0], stream)),
+           "bitlinear_quantize_acts_grouped")
+
+
+def bitlinear_forward(Xq, x_scale, W_packed, w_scale, Y, acc=None, stream=None):
+    T, K = Xq.shape
+    N = W_packed.shape[0]
+    _check(_c_fw(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, _ptr(Y),
+                 _ptr(acc), _stream(Xq, stream)), "bitlinear_forward")
+
+
+def bitlinear_forward_ex(Xq, x_scale, W_packed, w_scale, Y, acc=None, kernel="auto",
+                         stream=None):
+    T, K = Xq.shape
+    N = W_packed.shape[0]
+    k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check(_c_fwx(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, _ptr(Y),
+                  _ptr(acc), k, _stream(Xq, stream)), "bitlinear_forward_ex")
+
+
+def bitlinear_forward_choice(T: int, N: int, K: int) -> str:
+    return _KERNEL_NAMES[_c_choice(T, N, K)]
+
+
+def bitlinear_forward_grouped(entries, T, stream=None):
+    """entries: list of (Xq, x_scale, W_packed, w_scale, Y, acc_or_None)."""
+    arr = (_ProjDesc * len(entries))()
+    for i, (Xq, xs, Wp, ws, Y, acc) in enumerate(entries):
+        arr[i] = _ProjDesc(Xq.data_ptr(), xs.data_ptr(), Wp.data_ptr(), ws.data_ptr(),
+                           Y.data_ptr(), None if acc is None else acc.data_ptr(),
+                           Wp.shape[0], Xq.shape[-1])
+    _check(_c_fwg(arr, len(entries), T, _stream(entries[0][0], stream)),
+           "bitlinear_forward_grouped")
+
+
+# ---------------------------------------------------------------- allocating wrappers
+
+def quantize_weights(W: torch.Tensor, with_gamma: bool = False):
+    """W fp32 [N, K] on the GPU -> (packed uint8 [N, K/4], beta fp32 [1][, gamma fp64 [1]])."""
+    N, K = W.shape
+    dev = W.device
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    gamma = torch.empty(1, dtype=torch.float64, device=dev) if with_gamma else None
+    ws = torch.empty(bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    bitlinear_quantize_weights(W, packed, beta, gamma, ws)
+    return (packed, beta, gamma) if with_gamma else (packed, beta)
+
+
+def quantize_acts(X: torch.Tensor, gain=None, eps: float = 1e-6, flags: int = 0):
+    """X fp32 [T, K] -> (Xq int8 [T, K], x_scale fp32 [T])."""
+    T, K = X.shape
+    Xq = torch.empty((T, K), dtype=torch.int8, device=X.device)
+    xs = torch.empty(T, dtype=torch.float32, device=X.device)
+    bitlinear_quantize_acts(X, gain, eps, flags, Xq, xs)
+    return Xq, xs
+
+
+def forward(Xq, x_scale, packed, beta, with_acc: bool = False, kernel="auto"):
+    """(Xq [T, K], x_scale [T], packed [N, K/4], beta [1]) -> Y fp32 [T, N] (and acc)."""
+    T = Xq.shape[0]
+    N = packed.shape[0]
+    Y = torch.empty((T, N), dtype=torch.float32, device=Xq.device)
+    acc = torch.empty((T, N), dtype=torch.int32, device=Xq.device) if with_acc else None
+    bitlinear_forward_ex(Xq, x_scale, packed, beta, Y, acc, kernel)
+    return (Y, acc) if with_acc else Y
+
+
+class BitLinear(torch.nn.Module):
+    """A drop-in inference replacement of nn.Linear (no bias): weights quantized once
+    to packed ternary codes, activations RMSNorm'd and int8-quantized per call."""
+
+    def __init__(self, weight: torch.Tensor, eps: float = 1e-6, gain=None):
+        super().__init__()
+        packed, beta = quantize_weights(weight.detach().to(torch.float32).contiguous())
+        self.register_buffer("packed", packed)
+        self.register_buffer("beta", beta)
+        self.register_buffer("gain", None if gain is None else gain.to(torch.float32).contiguous())
+        self.eps = eps
+        self.in_features = weight.shape[1]
+        self.out_features = weight.shape[0]
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        shape = x.shape
+        x2 = x.reshape(-1, shape[-1]).to(torch.float32).contiguous()
+        Xq, xs = quantize_acts(x2, self.gain, self.eps)
+        y = forward(Xq, xs, self.packed, self.beta)
+        return y.reshape(*shape[:-1], self.out_features)

@@ -1,0 +1,203 @@
+// bl_capi.hip -- the C ABI of libbitlinear.so (declared in include/bitlinear.h):
+// host-side argument validation, kernel dispatch, status reporting. No C++ exception
+// crosses the ABI; nothing here allocates device memory or synchronizes the stream.
+#include <math.h>
+#include <string.h>
+
+#include "bl_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+bl_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return BL_OK;
+  const char* s = hipGetErrorString(e);
+  strncpy(g_last_error, s ? s : "unknown HIP error", sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = '\0';
+  return BL_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned_n(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
+constexpr int64_t kMaxRows = 0x7FFFFFFF;  // N, T fit an int
+constexpr int64_t kMaxTokens = 65535;
+constexpr int64_t kMaxWeights = int64_t(1) << 31;  // exact-sum digit capacity
+
+bl_status check_acts(const float* X, const float* gain, int64_t T, int64_t K, int8_t* Xq,
+                     float* xs) {
+  if (!X || !Xq || !xs) return BL_ERR_NULL;
+  if (T <= 0 || K <= 0 || K % 4 || T > kMaxTokens) return BL_ERR_DIM;
+  if (K > BL_MAX_K) return BL_ERR_K_TOO_LARGE;
+  if (!aligned16(X) || !aligned16(Xq) || !aligned_n(xs, 4) || (gain && !aligned_n(gain, 4)))
+    return BL_ERR_ALIGN;
+  return BL_OK;
+}
+
+bl_status check_proj(const int8_t* Xq, const float* xs, int64_t T, int64_t K,
+                     const uint8_t* W, const float* ws, int64_t N, float* Y, int32_t* acc) {
+  if (!Xq || !xs || !W || !ws || !Y) return BL_ERR_NULL;
+  if (T <= 0 || N <= 0 || K <= 0 || K % 4 || T > kMaxTokens || N > kMaxRows) return BL_ERR_DIM;
+  if (K > BL_MAX_K) return BL_ERR_K_TOO_LARGE;
+  if (!aligned16(Xq) || !aligned16(W) || !aligned16(Y) || (acc && !aligned16(acc)) ||
+      !aligned_n(xs, 4) || !aligned_n(ws, 4))
+    return BL_ERR_ALIGN;
+  return BL_OK;
+}
+
+bl_kernel choose(int64_t T, int64_t N, int64_t K) {
+  (void)N;
+  if (bl_gemv_supports((int)T, (int)K) && T <= 2) return BL_KERNEL_GEMV;
+  if (T <= 64 && bl_skinny_supports((int)T, (int)K)) return BL_KERNEL_SKINNY;
+  if (T > 64 && bl_prefill_supports((int)T, (int)K)) return BL_KERNEL_PREFILL;
+  if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
+  return BL_KERNEL_GENERIC;
+}
+
+bool supports(bl_kernel k, int64_t T, int64_t K) {
+  switch (k) {
+    case BL_KERNEL_GEMV: return bl_gemv_supports((int)T, (int)K);
+    case BL_KERNEL_SKINNY: return bl_skinny_supports((int)T, (int)K);
+    case BL_KERNEL_PREFILL: return bl_prefill_supports((int)T, (int)K);
+    case BL_KERNEL_GENERIC: return true;
+    default: return false;
+  }
+}
+
+bl_proj_internal to_internal(const int8_t* Xq, const float* xs, int64_t K, const uint8_t* W,
+                             const float* ws, int64_t N, float* Y, int32_t* acc) {
+  return bl_proj_internal{Xq, xs, W, ws, Y, acc, (int)N, (int)K};
+}
+
+hipError_t run(bl_kernel k, const bl_proj_internal* p, int count, int T, hipStream_t s) {
+  switch (k) {
+    case BL_KERNEL_GEMV: return bl_launch_gemv(p, count, T, s);
+    case BL_KERNEL_SKINNY: return bl_launch_skinny(p, count, T, s);
+    case BL_KERNEL_PREFILL:
+      for (int i = 0; i < count; ++i) {
+        hipError_t e = bl_launch_prefill(p + i, T, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    default:
+      for (int i = 0; i < count; ++i) {
+        hipError_t e = bl_launch_generic(p + i, T, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_weight_workspace_bytes(int64_t N, int64_t K) {
+  return bl_weight_workspace_bytes_impl(N, K);
+}
+
+bl_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed,
+                                     float* w_scale, double* w_gamma, void* workspace,
+                                     size_t workspace_bytes, bl_stream_t stream) {
+  if (!W || !W_packed || !w_scale) return BL_ERR_NULL;
+  if (N <= 0 || K <= 0 || K % 4 || N > kMaxRows || N * K > kMaxWeights) return BL_ERR_DIM;
+  if (!workspace || workspace_bytes < bitlinear_weight_workspace_bytes(N, K))
+    return BL_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(workspace) || !aligned_n(w_scale, 4) ||
+      (w_gamma && !aligned_n(w_gamma, 8)))
+    return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_quantize_weights(W, N, K, W_packed, w_scale, w_gamma, workspace,
+                                               (hipStream_t)stream));
+}
+
+bl_status bitlinear_quantize_acts(const float* X, const float* gain, int64_t T, int64_t K,
+                                  float eps, uint32_t flags, int8_t* Xq, float* x_scale,
+                                  bl_stream_t stream) {
+  bl_act_desc d{X, gain, Xq, x_scale, K};
+  return bitlinear_quantize_acts_grouped(&d, 1, T, eps, flags, stream);
+}
+
+bl_status bitlinear_quantize_acts_grouped(const bl_act_desc* descs, int count, int64_t T,
+                                          float eps, uint32_t flags, bl_stream_t stream) {
+  if (!descs) return BL_ERR_NULL;
+  if (count < 1 || count > BL_MAX_GROUP) return BL_ERR_ARG;
+  if ((flags & ~BL_NO_NORM) != 0u) return BL_ERR_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return BL_ERR_ARG;
+  for (int i = 0; i < count; ++i) {
+    bl_status s = check_acts(descs[i].X, descs[i].gain, T, descs[i].K, descs[i].Xq,
+                             descs[i].x_scale);
+    if (s != BL_OK) return s;
+  }
+  (void)hipGetLastError();
+  return hip_status(bl_launch_quantize_acts(descs, count, T, eps, flags, (hipStream_t)stream));
+}
+
+bl_kernel bitlinear_forward_choice(int64_t T, int64_t N, int64_t K) { return choose(T, N, K); }
+
+bl_status bitlinear_forward_ex(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                               const uint8_t* W_packed, const float* w_scale, int64_t N,
+                               float* Y, int32_t* acc, bl_kernel kernel, bl_stream_t stream) {
+  bl_status s = check_proj(Xq, x_scale, T, K, W_packed, w_scale, N, Y, acc);
+  if (s != BL_OK) return s;
+  if (kernel == BL_KERNEL_AUTO) kernel = choose(T, N, K);
+  if (!supports(kernel, T, K)) return BL_ERR_ARG;
+  bl_proj_internal p = to_internal(Xq, x_scale, K, W_packed, w_scale, N, Y, acc);
+  (void)hipGetLastError();
+  return hip_status(run(kernel, &p, 1, (int)T, (hipStream_t)stream));
+}
+
+bl_status bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                            const uint8_t* W_packed, const float* w_scale, int64_t N, float* Y,
+                            int32_t* acc, bl_stream_t stream) {
+  return bitlinear_forward_ex(Xq, x_scale, T, K, W_packed, w_scale, N, Y, acc, BL_KERNEL_AUTO,
+                              stream);
+}
+
+bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_t T,
+                                    bl_stream_t stream) {
+  if (!descs) return BL_ERR_NULL;
+  if (count < 1 || count > BL_MAX_GROUP) return BL_ERR_ARG;
+  bl_proj_internal p[BL_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    const bl_proj_desc& d = descs[i];
+    bl_status s = check_proj(d.Xq, d.x_scale, T, d.K, d.W_packed, d.w_scale, d.N, d.Y, d.acc);
+    if (s != BL_OK) return s;
+    p[i] = to_internal(d.Xq, d.x_scale, d.K, d.W_packed, d.w_scale, d.N, d.Y, d.acc);
+  }
+  (void)hipGetLastError();
+  // one launch per kernel kind: entries sharing the kernel choice go together
+  bl_proj_internal batch[BL_MAX_GROUP];
+  const bl_kernel kinds[4] = {BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_PREFILL,
+                              BL_KERNEL_GENERIC};
+  for (bl_kernel k : kinds) {
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+      if (choose(T, descs[i].N, descs[i].K) == k) batch[n++] = p[i];
+    if (n == 0) continue;
+    bl_status s = hip_status(run(k, batch, n, (int)T, (hipStream_t)stream));
+    if (s != BL_OK) return s;
+  }
+  return BL_OK;
+}
+
+const char* bitlinear_status_str(bl_status s) {
+  switch (s) {
+    case BL_OK: return "ok";
+    case BL_ERR_NULL: return "a required pointer is NULL";
+    case BL_ERR_DIM: return "invalid dimensions (T, N, K must be positive, K a multiple of 4)";
+    case BL_ERR_K_TOO_LARGE: return "K exceeds BL_MAX_K";
+    case BL_ERR_WORKSPACE: return "workspace missing or too small";
+    case BL_ERR_ALIGN: return "pointer not aligned as required";
+    case BL_ERR_HIP: return "HIP error";
+    case BL_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+const char* bitlinear_last_hip_error(void) { return g_last_error; }
+
+int bitlinear_abi_version(void) { return BL_ABI_VERSION; }
+
+}  // extern "C"

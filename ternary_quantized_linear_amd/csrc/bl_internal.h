@@ -1,0 +1,37 @@
+// bl_internal.h -- host-side launch functions shared between the kernel sources and
+// the C ABI (bl_capi.hip). Validation happens in the C ABI before any of these runs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+
+#define BL_GROUP_CAP BL_MAX_GROUP
+
+// One projection as the product kernels see it (host-validated, K % 4 == 0).
+struct bl_proj_internal {
+  const int8_t* Xq;
+  const float* x_scale;
+  const uint8_t* W;
+  const float* w_scale;
+  float* Y;
+  int32_t* acc;
+  int N;
+  int K;
+};
+
+size_t bl_weight_workspace_bytes_impl(int64_t N, int64_t K);
+hipError_t bl_launch_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* P,
+                                      float* w_scale, double* w_gamma, void* ws,
+                                      hipStream_t stream);
+hipError_t bl_launch_quantize_acts(const bl_act_desc* d, int count, int64_t T, float eps,
+                                   uint32_t flags, hipStream_t stream);
+
+// Product kernels: each takes 1..BL_GROUP_CAP projections sharing T.
+bool bl_gemv_supports(int T, int K);
+hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream);
+bool bl_skinny_supports(int T, int K);
+hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream);
+bool bl_prefill_supports(int T, int K);
+hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream);
+hipError_t bl_launch_generic(const bl_proj_internal* p, int T, hipStream_t stream);

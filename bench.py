@@ -1,0 +1,412 @@
+#!/usr/bin/env python
+"""Benchmark of the BitNet b1.58 BitLinear forward on one MI355X.
+
+Headline (one JSON line on stdout): decode GB/s of one Llama-3-8B layer at T = 1 --
+the seven projections q, k, v, o, gate, up, down -- as % of the 8 TB/s HBM peak.
+A step is one pass of the per-token hot path over that layer: one grouped launch of
+the fused RMSNorm + absmax int8 quantizer (four distinct inputs: attention input,
+attention output, MLP input, MLP middle; attention itself is excluded) and one grouped
+launch of the ternary GEMV over the seven projections. Weight quantization runs once
+before timing (it is the offline conversion step) and is timed separately. Steps
+cycle through 32 distinct copies of the packed layer (1.75 GB) so that the 256 MB
+last-level cache cannot serve repeated weights; steps are replayed from a HIP graph.
+
+Also reported, as extra objects of the same line: prefill int8 TOPS (T = 2048,
+(N, K) = (14336, 4096) and (4096, 14336)) as % of the 5.0 POPS int8 MFMA peak; the
+70B-shape token sweep; the full 32-layer x 7-projection pass at T = 16; the weight
+quantizer; and the CPU oracle on a bounded sample of the decode workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+METRIC = "BitLinear decode GB/s (% HBM peak) and prefill int8 TOPS (% MFMA peak)"
+REPLICAS = 32
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-decode", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy kernel (counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- timing helpers
+
+def _warm_then_capture(torch, fns):
+    """Run fns once eagerly (first-launch setup happens outside capture), then capture
+    them, in order, into one HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns[: min(len(fns), 4)]:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_graph(torch, g, reps=1):
+    """Average ms per replay of graph g, from HIP events on the replay stream."""
+    st = torch.cuda.Event(enable_timing=True)
+    en = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(reps):
+        g.replay()
+    en.record()
+    en.synchronize()
+    return st.elapsed_time(en) / reps
+
+
+def gemv_bytes(T, N, K):
+    """Algorithmic bytes of one projection's product: packed W, Xq, token scales,
+    beta, fp32 outputs."""
+    return N * K // 4 + T * K + 4 * T + 4 + 4 * T * N
+
+
+def act_bytes(T, K):
+    """Algorithmic bytes of one activation quantization: fp32 in, int8 + scale out."""
+    return 4 * T * K + T * K + 4 * T
+
+
+# ---------------------------------------------------------------- decode8b (headline)
+
+def setup_decode(torch, bl, workloads, T=1):
+    dev = torch.device("cuda:0")
+    Ws = workloads.decode8b_layer(0)
+    base = {}
+    for name, W in Ws.items():
+        base[name] = bl.quantize_weights(torch.from_numpy(W).to(dev))
+    torch.cuda.synchronize()
+    # distinct copies of the packed layer (same content, distinct HBM addresses)
+    reps = [base] + [{n: (p.clone(), b.clone()) for n, (p, b) in base.items()}
+                     for _ in range(REPLICAS - 1)]
+    inputs = workloads.decode8b_inputs(T, 100)
+    acts = {}
+    act_entries = []
+    for name, X in inputs.items():
+        Xg = torch.from_numpy(X).to(dev)
+        Xq = torch.empty(X.shape, dtype=torch.int8, device=dev)
+        xs = torch.empty(T, dtype=torch.float32, device=dev)
+        acts[name] = (Xq, xs)
+        act_entries.append((Xg, None, Xq, xs))
+    qa = bl.prepare_quantize_acts_grouped(act_entries, T)
+    outs = {p: torch.empty((T, N), dtype=torch.float32, device=dev)
+            for p, (N, K) in workloads.LLAMA3_8B.items()}
+    fws = []
+    for r in reps:
+        entries = []
+        for name, projs in workloads.LLAMA3_8B_INPUTS.items():
+            Xq, xs = acts[name]
+            for p in projs:
+                pk, b = r[p]
+                entries.append((Xq, xs, pk, b, outs[p], None))
+        fws.append(bl.prepare_forward_grouped(entries, T))
+    gemv_b = sum(gemv_bytes(T, N, K) for (N, K) in workloads.LLAMA3_8B.values())
+    act_b = sum(act_bytes(T, workloads.LLAMA3_8B[ps[0]][1])
+                for ps in workloads.LLAMA3_8B_INPUTS.values())
+    packed_b = sum(N * K // 4 for (N, K) in workloads.LLAMA3_8B.values())
+    return {"qa": qa, "fws": fws, "gemv_bytes": gemv_b, "act_bytes": act_b,
+            "packed_bytes": packed_b, "reps": reps, "Ws": Ws, "inputs": inputs}
+
+
+def run_decode(torch, d, steps, warmup):
+    qa, fws = d["qa"], d["fws"]
+
+    def step_fns(n, offset=0):
+        out = []
+        for i in range(n):
+            f = fws[(offset + i) % len(fws)]
+            out += [qa, f]
+        return out
+
+    g_warm = _warm_then_capture(torch, step_fns(max(warmup, 1)))
+    g_main = _warm_then_capture(torch, step_fns(steps, warmup))
+    if warmup > 0:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    ms_total = _time_graph(torch, g_main, 1)
+    ms_step = ms_total / steps
+    # the dominant kernel alone: 256 back-to-back grouped GEMV launches, graph-replayed
+    n_k = 256
+    g_k = _warm_then_capture(torch, [fws[i % len(fws)] for i in range(n_k)])
+    g_k.replay()
+    ms_gemv = _time_graph(torch, g_k, 2) / n_k
+    g_a = _warm_then_capture(torch, [qa] * 128)
+    g_a.replay()
+    ms_act = _time_graph(torch, g_a, 2) / 128
+    # eager launches (no graph), for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for f in step_fns(64):
+        f()
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / 64
+    return {"ms_step": ms_step, "ms_gemv": ms_gemv, "ms_act": ms_act, "ms_eager": ms_eager}
+
+
+# ---------------------------------------------------------------- extra workloads
+
+def run_prefill(torch, bl, workloads):
+    dev = torch.device("cuda:0")
+    T = workloads.PREFILL_T
+    out = []
+    for (N, K) in workloads.PREFILL_SHAPES:
+        W = torch.from_numpy(workloads.weights(N, K, 7)).to(dev)
+        packed, beta = bl.quantize_weights(W)
+        del W
+        Xs = [torch.from_numpy(workloads.acts_student_t(T, K, 8 + i)).to(dev) for i in range(4)]
+        Xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+        xs = torch.empty(T, dtype=torch.float32, device=dev)
+        Y = torch.empty((T, N), dtype=torch.float32, device=dev)
+        qas = [bl.prepare_quantize_acts_grouped([(X, None, Xq, xs)], T) for X in Xs]
+        fw = bl.prepare_forward_grouped([(Xq, xs, packed, beta, Y, None)], T)
+        qas[0]()
+        g = _warm_then_capture(torch, [fw] * 20)
+        g.replay()
+        ms = _time_graph(torch, g, 3) / 20
+        ga = _warm_then_capture(torch, [qas[i % 4] for i in range(16)])
+        ga.replay()
+        ms_a = _time_graph(torch, ga, 3) / 16
+        ops = 2.0 * T * N * K
+        tops = ops / (ms * 1e-3) / 1e12
+        out.append({"T": T, "N": N, "K": K, "kernel": bl.bitlinear_forward_choice(T, N, K),
+                    "ms": round(ms, 5), "tops": round(tops, 1),
+                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                    "act_quant_ms": round(ms_a, 5),
+                    "act_quant_gbs": round(act_bytes(T, K) / (ms_a * 1e-3) / 1e9, 1)})
+        del Xs, Xq, Y, packed
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_sweep70b(torch, bl, workloads):
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    out = []
+    for which, (N, K) in workloads.LLAMA_70B_SWEEP.items():
+        gen.manual_seed(70)
+        W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * workloads.WEIGHT_SIGMA
+        packed, beta = bl.quantize_weights(W)
+        del W
+        reps = [packed] + [packed.clone() for _ in range(7)]   # 8 x 58.7 MB > last-level cache
+        for T in workloads.SWEEP_TOKENS:
+            X = torch.from_numpy(workloads.acts_normal(T, K, 1000 + T)).to(dev)
+            Xq, xs = bl.quantize_acts(X)
+            Y = torch.empty((T, N), dtype=torch.float32, device=dev)
+            fws = [bl.prepare_forward_grouped([(Xq, xs, p, beta, Y, None)], T) for p in reps]
+            g = _warm_then_capture(torch, [fws[i % 8] for i in range(64)])
+            g.replay()
+            ms = _time_graph(torch, g, 2) / 64
+            b = gemv_bytes(T, N, K)
+            gbs = b / (ms * 1e-3) / 1e9
+            out.append({"proj": which, "N": N, "K": K, "T": T,
+                        "kernel": bl.bitlinear_forward_choice(T, N, K), "us": round(ms * 1e3, 2),
+                        "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "tops": round(2.0 * T * N * K / (ms * 1e-3) / 1e12, 2)})
+        del reps, packed
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_fullpass(torch, bl, workloads):
+    dev = torch.device("cuda:0")
+    T = workloads.FULLPASS_T
+    gen = torch.Generator(device=dev)
+    fns = []
+    keep = []
+    total_b = 0
+    for layer in range(workloads.LLAMA3_8B_LAYERS):
+        packed = {}
+        for i, (p, (N, K)) in enumerate(workloads.LLAMA3_8B.items()):
+            gen.manual_seed(layer * 16 + i)
+            W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * workloads.WEIGHT_SIGMA
+            packed[p] = bl.quantize_weights(W)
+            del W
+            total_b += gemv_bytes(T, N, K)
+        act_entries, acts = [], {}
+        for j, (name, ps) in enumerate(workloads.LLAMA3_8B_INPUTS.items()):
+            K = workloads.LLAMA3_8B[ps[0]][1]
+            X = torch.from_numpy(workloads.acts_normal(T, K, 5000 + 8 * layer + j)).to(dev)
+            Xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+            xs = torch.empty(T, dtype=torch.float32, device=dev)
+            act_entries.append((X, None, Xq, xs))
+            acts[name] = (Xq, xs)
+            total_b += act_bytes(T, K)
+        entries = []
+        for name, ps in workloads.LLAMA3_8B_INPUTS.items():
+            for p in ps:
+                N = workloads.LLAMA3_8B[p][0]
+                Y = torch.empty((T, N), dtype=torch.float32, device=dev)
+                entries.append((acts[name][0], acts[name][1], packed[p][0], packed[p][1], Y, None))
+        fns += [bl.prepare_quantize_acts_grouped(act_entries, T),
+                bl.prepare_forward_grouped(entries, T)]
+        keep.append((packed, act_entries, entries))
+    torch.cuda.synchronize()
+    g = _warm_then_capture(torch, fns)
+    g.replay()
+    ms = _time_graph(torch, g, 5)
+    gbs = total_b / (ms * 1e-3) / 1e9
+    res = {"layers": workloads.LLAMA3_8B_LAYERS, "T": T, "ms_per_pass": round(ms, 4),
+           "tokens_per_s": round(T / (ms * 1e-3), 1), "gbs": round(gbs, 1),
+           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "kernel": bl.bitlinear_forward_choice(T, 4096, 4096)}
+    del keep
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_weight_quant(torch, bl, workloads):
+    dev = torch.device("cuda:0")
+    N, K = workloads.LLAMA_70B_SWEEP["down"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * workloads.WEIGHT_SIGMA
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(bl.bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    f = lambda: bl.bitlinear_quantize_weights(W, packed, beta, None, ws)  # noqa: E731
+    g = _warm_then_capture(torch, [f] * 4)
+    g.replay()
+    ms = _time_graph(torch, g, 2) / 4
+    n = N * K
+    res = {"N": N, "K": K, "ms": round(ms, 4),
+           "gbs_algorithmic": round(4.25 * n / (ms * 1e-3) / 1e9, 1),
+           "gbs_two_pass": round(8.25 * n / (ms * 1e-3) / 1e9, 1)}
+    del W, packed, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_calib_copy(torch):
+    n = 64 * 1024 * 1024  # 256 MiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)   # one elementwise kernel: reads 256 MiB, writes 256 MiB
+    torch.cuda.synchronize()
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "kernel": "torch elementwise mul"}
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def run_cpu_baseline(d, workloads, budget_s=12.0):
+    import numpy as np  # noqa: F401
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    used = oracle.set_threads(cores)
+    packed = {p: oracle.quantize_weights(W)[:2] for p, W in d["Ws"].items()}
+    inputs = d["inputs"]
+    T = next(iter(inputs.values())).shape[0]
+
+    def one_step():
+        for name, ps in workloads.LLAMA3_8B_INPUTS.items():
+            Xq, s = oracle.quantize_acts(inputs[name])
+            for p in ps:
+                P, beta = packed[p]
+                oracle.forward(Xq, s, P, beta)
+
+    one_step()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    ms = el * 1e3 / n
+    b = d["gemv_bytes"] + d["act_bytes"]
+    return {"value": round(b / (ms * 1e-3) / 1e9, 3), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": "%d passes of the decode8b step (T=%d: act-quant of 4 inputs + 7 "
+                      "projections), %.1f s wall, %.2f ms/step" % (n, T, el, ms)}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the BitLinear path here has no multi-GPU "
+              "mode (requested --gpus %d, WORLD_SIZE %d)" % (a.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if a.steps < 1 or a.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import ternary_quantized_linear_amd as bl
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    T = 1
+    d = setup_decode(torch, bl, workloads, T)
+    r = run_decode(torch, d, a.steps, a.warmup)
+    step_bytes = d["gemv_bytes"] + d["act_bytes"]
+    value = step_bytes / (r["ms_step"] * 1e-3) / 1e9
+    achieved = d["gemv_bytes"] / (r["ms_gemv"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic: seeded 0.02*N(0,1) weights (absmean-ternarized, 2-bit packed), "
+                "N(0,1) activations",
+        "config": {"workload": "decode8b: one Llama-3-8B layer (q,k,v,o,gate,up,down) at T=1; "
+                               "step = grouped RMSNorm+int8 act-quant (4 inputs) + grouped "
+                               "ternary GEMV (7 projections); 32 rotating packed-weight "
+                               "replicas; HIP-graph replay",
+                   "T": T, "projections": 7, "packed_bytes_per_layer": d["packed_bytes"],
+                   "bytes_per_step": step_bytes, "frac_hbm_step": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1> (grouped, 7 projections)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": d["gemv_bytes"],
+                     "avg_launch_us": round(r["ms_gemv"] * 1e3, 3)},
+        "act_quant": {"avg_launch_us": round(r["ms_act"] * 1e3, 3),
+                      "bytes_per_launch": d["act_bytes"]},
+        "eager_ms_per_step": round(r["ms_eager"], 4),
+    }
+    del d["reps"]
+    if not a.only_decode:
+        line["prefill"] = run_prefill(torch, bl, workloads)
+        line["sweep70b"] = run_sweep70b(torch, bl, workloads)
+        line["fullpass"] = run_fullpass(torch, bl, workloads)
+        line["weight_quant"] = run_weight_quant(torch, bl, workloads)
+    if a.calib_copy:
+        line["calib_copy"] = run_calib_copy(torch)
+    line["cpu_baseline"] = None if a.no_cpu else run_cpu_baseline(d, workloads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

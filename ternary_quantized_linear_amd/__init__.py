@@ -23,6 +23,7 @@ __all__ = [
     "bitlinear_forward_choice", "bitlinear_forward_grouped", "bitlinear_status_str",
     "bitlinear_last_hip_error", "bitlinear_abi_version", "quantize_weights",
     "quantize_acts", "forward", "BitLinear", "KERNELS", "NO_NORM", "MAX_K", "MAX_GROUP",
+    "prepare_forward_grouped", "prepare_quantize_acts_grouped",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -172,6 +173,39 @@ def bitlinear_forward_grouped(entries, T, stream=None):
                            Wp.shape[0], Xq.shape[-1])
     _check(_c_fwg(arr, len(entries), T, _stream(entries[0][0], stream)),
            "bitlinear_forward_grouped")
+
+
+class PreparedCall:
+    """A grouped ABI call with its descriptor array marshalled once. Calling it
+    launches on the current stream at call time (so it can be captured into a graph)."""
+
+    def __init__(self, fn, arr, count, T, extra, where, keep):
+        self._fn, self._arr, self._count, self._T = fn, arr, count, T
+        self._extra, self._where, self._keep = extra, where, keep
+
+    def __call__(self, stream=None):
+        s = _stream(self._keep[0], stream)
+        _check(self._fn(self._arr, self._count, self._T, *self._extra, s), self._where)
+
+
+def prepare_quantize_acts_grouped(entries, T, eps=1e-6, flags=0):
+    arr = (_ActDesc * len(entries))()
+    for i, (X, gain, Xq, xs) in enumerate(entries):
+        arr[i] = _ActDesc(X.data_ptr(), None if gain is None else gain.data_ptr(), Xq.data_ptr(),
+                          xs.data_ptr(), X.shape[-1])
+    keep = [t for e in entries for t in e if t is not None]
+    return PreparedCall(_c_qag, arr, len(entries), T, (ctypes.c_float(eps), ctypes.c_uint32(flags)),
+                        "bitlinear_quantize_acts_grouped", keep)
+
+
+def prepare_forward_grouped(entries, T):
+    arr = (_ProjDesc * len(entries))()
+    for i, (Xq, xs, Wp, ws, Y, acc) in enumerate(entries):
+        arr[i] = _ProjDesc(Xq.data_ptr(), xs.data_ptr(), Wp.data_ptr(), ws.data_ptr(),
+                           Y.data_ptr(), None if acc is None else acc.data_ptr(),
+                           Wp.shape[0], Xq.shape[-1])
+    keep = [t for e in entries for t in e if t is not None]
+    return PreparedCall(_c_fwg, arr, len(entries), T, (), "bitlinear_forward_grouped", keep)
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -223,14 +223,16 @@ int gemv_rows_per_block(int K) {
   return r < 16 ? 16 : (r > 256 ? 256 : r);
 }
 
+constexpr int kGemvMaxLds = 96 * 1024;
+
+// The dynamic-LDS limit is raised once per instance (the first launch on the device),
+// so no attribute call happens inside a stream capture after that.
 template <int TT>
 hipError_t launch_gemv_t(dim3 grid, dim3 block, size_t lds, hipStream_t stream,
                          const GemvArgs& a) {
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemv_kernel<TT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)gemv_kernel<TT>, hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxLds);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(gemv_kernel<TT>, grid, block, lds, stream, a);
   return hipGetLastError();
 }
@@ -241,7 +243,7 @@ using namespace bl;
 
 bool bl_gemv_supports(int T, int K) {
   if (T < 1 || T > 2 || K % 64) return false;
-  return (size_t)T * (K + 16) <= 96 * 1024;
+  return (size_t)T * (K + 16) <= (size_t)kGemvMaxLds;
 }
 
 hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream) {

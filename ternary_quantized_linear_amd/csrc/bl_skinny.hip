@@ -169,6 +169,19 @@ int skinny_chunk(int T, int K) {
   return 256 * best;
 }
 
+// The dynamic-LDS limit is raised once per instance (first launch), never inside a
+// stream capture after that.
+template <int TB>
+hipError_t launch_skinny_t(dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                           const SkArgs& a) {
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)skinny_kernel<TB>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkLdsBudget);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(skinny_kernel<TB>, grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace bl
 
 using namespace bl;
@@ -198,30 +211,10 @@ hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStre
   a.count = count;
   a.T = T;
   dim3 grid((unsigned)blocks), block(kSkThreads);
-  const int TB = (T + 15) / 16;
-  hipError_t e = hipSuccess;
-  switch (TB) {
-    case 1:
-      e = hipFuncSetAttribute((const void*)skinny_kernel<1>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e == hipSuccess) hipLaunchKernelGGL(skinny_kernel<1>, grid, block, lds, stream, a);
-      break;
-    case 2:
-      e = hipFuncSetAttribute((const void*)skinny_kernel<2>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e == hipSuccess) hipLaunchKernelGGL(skinny_kernel<2>, grid, block, lds, stream, a);
-      break;
-    case 3:
-      e = hipFuncSetAttribute((const void*)skinny_kernel<3>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e == hipSuccess) hipLaunchKernelGGL(skinny_kernel<3>, grid, block, lds, stream, a);
-      break;
-    default:
-      e = hipFuncSetAttribute((const void*)skinny_kernel<4>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e == hipSuccess) hipLaunchKernelGGL(skinny_kernel<4>, grid, block, lds, stream, a);
-      break;
+  switch ((T + 15) / 16) {
+    case 1: return launch_skinny_t<1>(grid, block, lds, stream, a);
+    case 2: return launch_skinny_t<2>(grid, block, lds, stream, a);
+    case 3: return launch_skinny_t<3>(grid, block, lds, stream, a);
+    default: return launch_skinny_t<4>(grid, block, lds, stream, a);
   }
-  if (e != hipSuccess) return e;
-  return hipGetLastError();
 }

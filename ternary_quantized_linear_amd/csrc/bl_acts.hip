@@ -36,6 +36,9 @@ struct ActArgs {
   int no_norm;
 };
 
+// Block-wide double-double sum. Each wave reduces its lanes with shuffles; after one
+// barrier every wave reduces the per-wave partials itself, in the same order, so all
+// waves hold the same bits without a second barrier.
 template <int NT>
 __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_hi,
                                              double* sh_lo) {
@@ -48,15 +51,15 @@ __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_
   }
   if (lane == 0) { sh_hi[wave] = hi; sh_lo[wave] = lo; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double h = sh_hi[0], l = sh_lo[0];
-    for (int w = 1; w < NW; ++w) dd_add(h, l, sh_hi[w], sh_lo[w]);
-    sh_hi[0] = h;
-    sh_lo[0] = l;
+  hi = lane < NW ? sh_hi[lane] : 0.0;
+  lo = lane < NW ? sh_lo[lane] : 0.0;
+#pragma unroll
+  for (int m = NW / 2; m >= 1; m >>= 1) {
+    double oh = __shfl_xor(hi, m, kWave), ol = __shfl_xor(lo, m, kWave);
+    dd_add(hi, lo, oh, ol);
   }
-  __syncthreads();
-  hi = sh_hi[0];
-  lo = sh_lo[0];
+  hi = __shfl(hi, 0, kWave);
+  lo = __shfl(lo, 0, kWave);
 }
 
 template <int NT>
@@ -66,10 +69,10 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
   v = wave_max_f32(v);
   if (lane == 0) sh[wave] = v;
   __syncthreads();
-  float m = sh[0];
+  float m = lane < NW ? sh[lane] : 0.0f;
 #pragma unroll
-  for (int w = 1; w < NW; ++w) m = fmaxf(m, sh[w]);
-  return m;
+  for (int k = NW / 2; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, kWave));
+  return __shfl(m, 0, kWave);
 }
 
 __device__ __forceinline__ float norm_one(float x, double r, const float* gain, int k) {
@@ -207,7 +210,16 @@ hipError_t bl_launch_quantize_acts(const bl_act_desc* d, int count, int64_t T, f
   a.no_norm = (flags & BL_NO_NORM) ? 1 : 0;
   dim3 grid((unsigned)T, (unsigned)count);
   const int f4 = (maxK + 3) / 4;  // float4 per row
-  // smallest register footprint that holds the longest row with 256 lanes
+  if (T <= 64) {
+    // few rows: latency-bound, so spread each row over 1024 lanes
+    if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<1024, 1>), grid, dim3(1024), 0, stream, a);
+    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<1024, 2>), grid, dim3(1024), 0, stream, a);
+    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<1024, 4>), grid, dim3(1024), 0, stream, a);
+    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<1024, 8>), grid, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL((act_quant_stream<1024>), grid, dim3(1024), 0, stream, a);
+    return hipGetLastError();
+  }
+  // many rows: throughput-bound; the smallest register footprint that holds the row
   if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1>), grid, dim3(256), 0, stream, a);
   else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2>), grid, dim3(256), 0, stream, a);
   else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4>), grid, dim3(256), 0, stream, a);

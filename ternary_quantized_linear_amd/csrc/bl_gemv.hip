@@ -1,5 +1,5 @@
-// bl_gemv.hip -- decode GEMV for T <= 2 tokens: packed ternary weights x int8
-// activations with int8 dot4 (v_dot4c_i32_i8), int32 accumulation, fused rescale.
+// bl_gemv.hip -- decode GEMV for one token: packed ternary weights x int8 activations
+// with int8 dot4 (v_dot4c_i32_i8), int32 accumulation, fused rescale.
 //
 // [HF-1.58] "Fine-tuning LLMs to 1.58 bits", "Computation paradigm": the ternary
 // product needs only integer additions; "Inference optimization and custom kernels":
@@ -8,27 +8,41 @@
 // operation": the integer product is rescaled by the weight scale and the activation
 // dequantization factor.
 //
-// Design (gfx950, wave64):
-//   - A workgroup (4 waves) owns a block of rows of one projection. It first stages the
-//     T activation rows into LDS, each 16-byte group 4x4 byte-transposed so that a
-//     dword of activations lines up with a dword of unpacked codes (transpose16 /
-//     unpack_u2), and sums each token's int8 values (sum_x).
-//   - A row of K codes is K/4 bytes = C chunks of 16 bytes (64 codes). L lanes cover a
-//     row (L = 64, 32 or 16, the largest that divides C), each lane streaming I = C/L
-//     chunks with 128-bit loads; 64/L rows are in flight per wave instruction.
-//   - Codes are used as u = q + 1 in {0, 1, 2} (no sign fix-up in the loop); the
-//     product is corrected once per row: acc = sum x*u - sum_x.
-//   - The L partial sums are reduced with DPP; Y = fp32(acc) * fp32(beta / s_t).
-// Several projections (for example the seven of a decoder layer, which read four
-// different inputs) go in one launch: the grid is the concatenation of their row
-// blocks.
+// For one token the product streams 1/4 byte per weight, so the design is about HBM:
+//   - A row of K codes is K/4 bytes = C chunks of 16 bytes (64 codes, one 128-bit load
+//     per lane). A row of up to 64 chunks is one wave's (L = 16 or 32 lanes per row when
+//     it has at most 16 or 32 chunks, so one wave instruction covers 64/L rows). A longer
+//     row is cut into S = 2 or 4 contiguous segments, read at the same time by S waves of
+//     one workgroup, each wave always taking the same segment: every wave keeps the
+//     activations of its own chunks in registers for the whole run. The S partial sums
+//     meet in one 64-bit LDS word (partial sum in the low bits, arrival count from bit
+//     40); the wave whose add completes the count writes the row.
+//   - Activations are 4x4 byte-transposed (transpose16) so that dword p of a chunk holds
+//     the codes in bit pair p of the four packed bytes. Lanes past the row end or past
+//     their segment hold zero activations, so whatever weights they read add nothing.
+//   - Workgroups are partitioned among the projections of the launch (for example the
+//     seven of a decoder layer) in proportion to their bytes; inside a partition the rows
+//     are swept grid-stride, so each partition reads one compact window of its matrix at
+//     a time. The grid is one round of resident workgroups. Each wave keeps D row groups
+//     of weights in flight in a ring of registers; a prefetch past the wave's last row
+//     reads a small L2-resident block instead, so no load sits under a branch and each
+//     step waits for exactly the oldest buffer.
+//   - The wave index is made explicitly uniform (readfirstlane): the whole schedule stays
+//     in scalar registers and the row bases are scalar.
+//   - Unpacking is 5 ALU ops per packed dword: bit pairs 0, 1, 2 are masked in place
+//     (values u, 4u, 16u with u = q + 1 in {0, 1, 2}) and pair 3 shifted down, each into
+//     its own dot4 accumulator; the sum is a0 + a1/4 + a2/16 + a3 (exact shifts of exact
+//     multiples) started at minus the lane's own activation sum: sum x*q exactly.
+//   - Lane sums are reduced with DPP; Y = fp32(acc) * fp32(beta / s).
 #include "bl_device.h"
 #include "bl_internal.h"
 
 namespace bl {
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kGemvWaves = kGemvThreads / kWave;  // 4
+constexpr int kGemvDepth = 4;                      // row groups in flight per wave
+constexpr int kGemvMaxC = 512;                     // K <= 32768
 
 struct GemvProj {
   const int8_t* Xq;
@@ -37,237 +51,286 @@ struct GemvProj {
   const float* ws;
   float* Y;
   int32_t* acc;
-  int N, K;
-  int blk0;     // first block index of this projection in the grid
-  int rows_pb;  // rows per block
-  int cfg;      // row-mapping variant (see gemv_kernel)
+  int N, C;
+  int wg0, nwg;  // this projection's workgroups
+  int cfg;       // mapping (see gemv_kernel)
+  int CW;        // chunks per wave segment
 };
 
 struct GemvArgs {
   GemvProj p[BL_GROUP_CAP];
   int count;
+  int slots;  // 64-bit combine words per workgroup (0: no segmented rows)
 };
 
-template <class E, int CAP>
-__device__ __forceinline__ E pick(const E (&arr)[CAP], int idx) {
-  E r = arr[0];
-#pragma unroll
-  for (int i = 1; i < CAP; ++i)
-    if (i == idx) r = arr[i];
-  return r;
+typedef const GemvArgs __attribute__((address_space(4)))* ArgsPtr;
+
+// Field-by-field copy out of the constant (kernel-argument) address space.
+__device__ __forceinline__ GemvProj load_proj(ArgsPtr a, int i) {
+  GemvProj P;
+  P.Xq = a->p[i].Xq;
+  P.xs = a->p[i].xs;
+  P.W = a->p[i].W;
+  P.ws = a->p[i].ws;
+  P.Y = a->p[i].Y;
+  P.acc = a->p[i].acc;
+  P.N = a->p[i].N;
+  P.C = a->p[i].C;
+  P.wg0 = a->p[i].wg0;
+  P.nwg = a->p[i].nwg;
+  P.cfg = a->p[i].cfg;
+  P.CW = a->p[i].CW;
+  return P;
 }
 
-// LDS layout of the staged activations: token t starts at byte t * (K + 16); inside a
-// token the 16-byte group 4c + d (chunk c, sub-group d) sits at slot d * C + c, so that
-// lanes reading consecutive chunks hit consecutive 16-byte slots.
-__device__ __forceinline__ int xslot(int t, int c, int d, int C, int tstride16) {
-  return t * tstride16 + d * C + c;
+// Four accumulators, one per bit pair (pairs 1 and 2 carry factors 4 and 16).
+struct Acc4 {
+  int a0, a1, a2, a3;
+};
+
+__device__ __forceinline__ void dot_word(uint32_t w, const uint4& x, Acc4& s) {
+  s.a0 = sdot4(w & 0x03030303u, x.x, s.a0);
+  s.a1 = sdot4(w & 0x0C0C0C0Cu, x.y, s.a1);
+  s.a2 = sdot4(w & 0x30303030u, x.z, s.a2);
+  s.a3 = sdot4((w >> 6) & 0x03030303u, x.w, s.a3);
 }
 
-template <int TT>
-__device__ __forceinline__ void stage_acts(const GemvProj& P, uint4* xl, int* sums) {
-  const int K = P.K, G = K >> 4, C = K >> 6, ts16 = G + 1;
-  int part[TT];
-#pragma unroll
-  for (int t = 0; t < TT; ++t) part[t] = 0;
-  for (int g = threadIdx.x; g < TT * G; g += kGemvThreads) {
-    const int t = g / G, gi = g - t * G;
-    const uint4 v = reinterpret_cast<const uint4*>(P.Xq + (int64_t)t * K)[gi];
-    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-    transpose16(a, o);
-    xl[xslot(t, gi >> 2, gi & 3, C, ts16)] = make_uint4(o[0], o[1], o[2], o[3]);
-    const int s = byte_sum(v.x) + byte_sum(v.y) + byte_sum(v.z) + byte_sum(v.w);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-      if (tt == t) part[tt] += s;
-  }
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int w = wave_sum_i32(part[t]);
-    if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&sums[t], w);
-  }
+__device__ __forceinline__ void dot_chunk(const uint4 w, const uint4 (&x)[4], Acc4& s) {
+  dot_word(w.x, x[0], s);
+  dot_word(w.y, x[1], s);
+  dot_word(w.z, x[2], s);
+  dot_word(w.w, x[3], s);
 }
 
-template <int TT>
-__device__ __forceinline__ void dot_chunk(const uint4 w, const uint4* xl, int c, int C,
-                                          int ts16, int (&acc)[TT]) {
-  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+__device__ __forceinline__ int acc_total(const Acc4& s) {
+  return s.a0 + s.a3 + (s.a1 >> 2) + (s.a2 >> 4);
+}
+
+// Activations of chunk c (64 codes): 4 x 16 bytes, transposed, and their sum; zeros when
+// the lane has no chunk.
+__device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, uint4 (&o)[4],
+                                               int& xsum) {
+  const uint4* src = reinterpret_cast<const uint4*>(x + 64 * c);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    uint32_t u[4];
-    unpack_u2(words[d], u);
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      const uint4 x = xl[xslot(t, c, d, C, ts16)];
-      int a = acc[t];
-      a = sdot4(u[0], x.x, a);
-      a = sdot4(u[1], x.y, a);
-      a = sdot4(u[2], x.z, a);
-      a = sdot4(u[3], x.w, a);
-      acc[t] = a;
-    }
+    uint4 v = src[d];
+    if (!on) v = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t t[4];
+    transpose16(in, t);
+    o[d] = make_uint4(t[0], t[1], t[2], t[3]);
+    xsum += byte_sum(v.x) + byte_sum(v.y) + byte_sum(v.z) + byte_sum(v.w);
   }
 }
 
-template <int TT, int L>
-__device__ __forceinline__ void finish_row(const GemvProj& P, int row, bool valid,
-                                           const int (&acc)[TT], const int* sums,
-                                           const float* fac) {
-  const int j = threadIdx.x & (L - 1);
+// One projection's partition. L lanes per row, I chunks per lane, S waves per row
+// (S > 1 needs L = 64). Wave `wave` of partition workgroup `wgl` takes segment wave % S
+// of row groups wgl * (4/S) + wave / S + k * stride, k = 0, 1, ...
+template <int L, int I, int S>
+__device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
+                                      unsigned long long* slots) {
+  constexpr int RW = kWave / L;        // rows per row group
+  constexpr int GPW = kGemvWaves / S;  // row groups per workgroup step
+  const int lane = threadIdx.x & (kWave - 1);
+  const int sub = lane / L, jl = lane & (L - 1);
+  const int C = P.C;
+  const int cw = S > 1 ? P.CW : C;  // chunks of this wave's segment
+  const int cbase = (wave % S) * cw;
+  const int ngroups = (P.N + RW - 1) / RW;
+  const int stride = P.nwg * GPW;
+  const int g0 = wgl * GPW + wave / S;
+  if (g0 >= ngroups) return;
+  const int glast = g0 + ((ngroups - 1 - g0) / stride) * stride;
+
+  // lane chunk i is cbase + jl + L*i when that is inside the segment and the row; a
+  // lane without a chunk reads its segment's first one (same cache line as lane 0)
+  int ci[I];
+  uint4 x[I][4];
+  int xsum = 0;
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int tot = group_sum_to_last<L>(acc[t]);
-    if (valid && j == L - 1) {
-      const int a = tot - sums[t];
-      P.Y[(int64_t)t * P.N + row] = (float)a * fac[t];
-      if (P.acc) P.acc[(int64_t)t * P.N + row] = a;
-    }
+  for (int i = 0; i < I; ++i) {
+    const int c = jl + L * i;
+    const bool on = c < cw && cbase + c < C;
+    ci[i] = on ? cbase + c : cbase;
+    load_act_chunk(P.Xq, ci[i], on, x[i], xsum);
   }
+  const uint4* dummy = reinterpret_cast<const uint4*>(P.Xq);  // 64 bytes, L2-resident
+  // the row group's base is wave-uniform (scalar); each lane adds a 32-bit offset
+  auto load_w = [&](int g, uint4 (&w)[I]) {
+    const bool real = g <= glast;
+    const int row0 = g * RW;
+    const uint4* base = real ? P.W + (int64_t)row0 * C : dummy;
+    const int off = real ? (min(row0 + sub, P.N - 1) - row0) * C : -1;
+#pragma unroll
+    for (int i = 0; i < I; ++i) w[i] = load_stream(base + (off < 0 ? (lane & 3) : off + ci[i]));
+  };
+  uint4 w[kGemvDepth][I];
+#pragma unroll
+  for (int d = 0; d < kGemvDepth; ++d) load_w(g0 + d * stride, w[d]);
+  const float f = P.ws[0] / P.xs[0];
+  int g = g0, k = 0;
+  // one row group: consume buffer d, refill it D groups ahead (prefetch), write the row
+  auto step = [&](int d, bool prefetch) {
+    Acc4 s{-xsum, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < I; ++i) dot_chunk(w[d][i], x[i], s);
+    if (prefetch) load_w(g + kGemvDepth * stride, w[d]);
+    int tot = group_sum_to_last<L>(acc_total(s));
+    const int row = g * RW + sub;
+    if ((lane & (L - 1)) == L - 1 && row < P.N) {
+      bool done = true;
+      if constexpr (S > 1) {
+        const unsigned long long mine = (1ull << 40) + (unsigned long long)(long long)tot;
+        const unsigned long long now = atomicAdd(&slots[k * GPW + wave / S], mine) + mine;
+        const unsigned long long n = (now + (1ull << 39)) >> 40;
+        done = n == (unsigned long long)S;
+        tot = (int)(long long)(now - (n << 40));
+      }
+      if (done) {
+        P.Y[row] = (float)tot * f;
+        if (P.acc) P.acc[row] = tot;
+      }
+    }
+    g += stride;
+    ++k;
+  };
+  // Whole rounds of D groups in a loop with a single exit, then the remaining groups
+  // (already in flight) straight-line: no exit in the middle of the ring, so the wait
+  // before each group is for its own buffer only.
+  int left = (glast - g0) / stride + 1;
+  while (left >= kGemvDepth) {
+#pragma unroll
+    for (int d = 0; d < kGemvDepth; ++d) step(d, true);
+    left -= kGemvDepth;
+  }
+#pragma unroll
+  for (int d = 0; d < kGemvDepth - 1; ++d)
+    if (d < left) step(d, false);
 }
 
-// Fixed mapping: C == L * I chunks per row, R row groups per wave iteration.
-template <int TT, int L, int I, int R>
-__device__ __forceinline__ void rows_fixed(const GemvProj& P, int row0, int row1,
-                                           const uint4* xl, const int* sums, const float* fac) {
-  constexpr int RW = kWave / L;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int sub = lane / L, j = lane & (L - 1);
-  const int C = P.K >> 6, ts16 = (P.K >> 4) + 1;
-  for (int rg = row0 + wave * RW * R; rg < row1; rg += kGemvWaves * RW * R) {
-    uint4 w[R][I];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(rg + r * RW + sub, row1 - 1);
-      const uint4* wr = P.W + (int64_t)row * C;
-#pragma unroll
-      for (int i = 0; i < I; ++i) w[r][i] = load_stream(wr + j + L * i);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int acc[TT];
-#pragma unroll
-      for (int t = 0; t < TT; ++t) acc[t] = 0;
-#pragma unroll
-      for (int i = 0; i < I; ++i) dot_chunk<TT>(w[r][i], xl, j + L * i, C, ts16, acc);
-      const int row = rg + r * RW + sub;
-      finish_row<TT, L>(P, row, row < row1, acc, sums, fac);
-    }
-  }
-}
-
-// Any K % 64 == 0: 64 lanes per row, ceil(C/64) masked iterations.
-template <int TT>
-__device__ __forceinline__ void rows_any(const GemvProj& P, int row0, int row1,
-                                         const uint4* xl, const int* sums, const float* fac) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int C = P.K >> 6, ts16 = (P.K >> 4) + 1;
-  for (int row = row0 + wave; row < row1; row += kGemvWaves) {
-    int acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0;
-    for (int c = lane; c < C; c += kWave) {
-      const uint4 w = load_stream(P.W + (int64_t)row * C + c);
-      dot_chunk<TT>(w, xl, c, C, ts16, acc);
-    }
-    finish_row<TT, 64>(P, row, true, acc, sums, fac);
-  }
-}
-
-template <int TT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
-  extern __shared__ uint4 smem[];
-  __shared__ int sums[TT];
-  __shared__ float fac[TT];
+// MAXI = 2 adds the mapping for rows of more than 256 chunks (two chunks per lane);
+// the MAXI = 1 instance leaves it out so that its register budget stays small.
+template <int MAXI>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
+  extern __shared__ unsigned long long slots[];
+  const ArgsPtr a = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  const int count = a->count;
+  const int wg = (int)blockIdx.x;
   int pi = 0;
-#pragma unroll
-  for (int i = 1; i < BL_GROUP_CAP; ++i)
-    if (i < a.count && (int)blockIdx.x >= a.p[i].blk0) pi = i;
-  const GemvProj P = pick(a.p, pi);
-  if (threadIdx.x < TT) {
-    sums[threadIdx.x] = 0;
-    fac[threadIdx.x] = P.ws[0] / P.xs[threadIdx.x];
+  for (int i = 1; i < count; ++i)
+    if (wg >= a->p[i].wg0) pi = i;
+  const GemvProj P = load_proj(a, pi);
+  // the wave index is uniform per wave: readfirstlane keeps the row schedule, the
+  // branches and the row bases in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wgl = wg - P.wg0;
+  if (P.cfg >= 3) {  // segmented rows: clear the combine words
+    for (int i = threadIdx.x; i < a->slots; i += kGemvThreads) slots[i] = 0ull;
+    __syncthreads();
   }
-  __syncthreads();
-  stage_acts<TT>(P, smem, sums);
-  __syncthreads();
-  const int row0 = ((int)blockIdx.x - P.blk0) * P.rows_pb;
-  const int row1 = min(row0 + P.rows_pb, P.N);
   switch (P.cfg) {
-    case 0: rows_fixed<TT, 64, 1, 4>(P, row0, row1, smem, sums, fac); break;  // C = 64
-    case 1: rows_fixed<TT, 64, 2, 2>(P, row0, row1, smem, sums, fac); break;  // C = 128
-    case 2: rows_fixed<TT, 32, 7, 1>(P, row0, row1, smem, sums, fac); break;  // C = 224
-    case 3: rows_fixed<TT, 64, 7, 1>(P, row0, row1, smem, sums, fac); break;  // C = 448
-    case 4: rows_fixed<TT, 16, 1, 4>(P, row0, row1, smem, sums, fac); break;  // C = 16
-    case 5: rows_fixed<TT, 32, 1, 4>(P, row0, row1, smem, sums, fac); break;  // C = 32
-    default: rows_any<TT>(P, row0, row1, smem, sums, fac); break;
+    case 0: sweep<16, 1, 1>(P, wgl, wave, slots); break;  // C <= 16
+    case 1: sweep<32, 1, 1>(P, wgl, wave, slots); break;  // C <= 32
+    case 2: sweep<64, 1, 1>(P, wgl, wave, slots); break;  // C <= 64
+    case 3: sweep<64, 1, 2>(P, wgl, wave, slots); break;  // C <= 128
+    case 4: sweep<64, 1, 4>(P, wgl, wave, slots); break;  // C <= 256
+    default:
+      if constexpr (MAXI >= 2) sweep<64, 2, 4>(P, wgl, wave, slots);  // C <= 512
+      break;
   }
 }
 
-int gemv_cfg(int K) {
-  switch (K >> 6) {
-    case 64: return 0;
-    case 128: return 1;
-    case 224: return 2;
-    case 448: return 3;
-    case 16: return 4;
-    case 32: return 5;
-    default: return 6;
+struct GemvCfg {
+  int cfg, S, RW;
+};
+
+GemvCfg gemv_cfg(int C) {
+  if (C <= 16) return {0, 1, 4};
+  if (C <= 32) return {1, 1, 2};
+  if (C <= 64) return {2, 1, 1};
+  if (C <= 128) return {3, 2, 1};
+  if (C <= 256) return {4, 4, 1};
+  return {5, 4, 1};
+}
+
+// Workgroups of one instance the device keeps resident at once (queried once per
+// instance; the combine words never take enough LDS to change it).
+int gemv_resident(bool big, size_t lds) {
+  static int cached[2] = {0, 0};
+  if (cached[big]) return cached[big];
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
   }
-}
-
-// Rows per workgroup: about 64 KiB of packed weights, a multiple of 16 rows.
-int gemv_rows_per_block(int K) {
-  int r = (64 * 1024) / (K / 4);
-  r = (r / 16) * 16;
-  return r < 16 ? 16 : (r > 256 ? 256 : r);
-}
-
-constexpr int kGemvMaxLds = 96 * 1024;
-
-// The dynamic-LDS limit is raised once per instance (the first launch on the device),
-// so no attribute call happens inside a stream capture after that.
-template <int TT>
-hipError_t launch_gemv_t(dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                         const GemvArgs& a) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)gemv_kernel<TT>, hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxLds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(gemv_kernel<TT>, grid, block, lds, stream, a);
-  return hipGetLastError();
+  int per = 0;
+  const void* f = big ? (const void*)gemv_kernel<2> : (const void*)gemv_kernel<1>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, kGemvThreads, lds) != hipSuccess ||
+      per < 1)
+    per = 2;
+  cached[big] = cus * per;
+  return cached[big];
 }
 
 }  // namespace bl
 
 using namespace bl;
 
-bool bl_gemv_supports(int T, int K) {
-  if (T < 1 || T > 2 || K % 64) return false;
-  return (size_t)T * (K + 16) <= (size_t)kGemvMaxLds;
-}
+bool bl_gemv_supports(int T, int K) { return T == 1 && K % 64 == 0 && K / 64 <= kGemvMaxC; }
 
 hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
+  (void)T;
   GemvArgs a{};
-  int blocks = 0, maxK = 0;
+  int64_t total = 0;
+  GemvCfg cfg[BL_GROUP_CAP];
+  bool big = false;
+  for (int i = 0; i < count; ++i) {
+    cfg[i] = gemv_cfg((int)(p[i].K / 64));
+    big = big || cfg[i].cfg == 5;
+    total += (int64_t)p[i].N * (p[i].K / 4);
+  }
+  // One round of resident workgroups (the combine words take at most a few KB of LDS);
+  // each projection gets workgroups in proportion to its bytes, at least one and never
+  // one without a row group.
+  const int cap = gemv_resident(big, 4096);
+  int wgs = 0, slots = 0;
   for (int i = 0; i < count; ++i) {
     GemvProj& g = a.p[i];
+    const GemvCfg c = cfg[i];
     g.Xq = p[i].Xq;
     g.xs = p[i].x_scale;
     g.W = reinterpret_cast<const uint4*>(p[i].W);
     g.ws = p[i].w_scale;
     g.Y = p[i].Y;
     g.acc = p[i].acc;
-    g.N = p[i].N;
-    g.K = p[i].K;
-    g.cfg = gemv_cfg(p[i].K);
-    g.rows_pb = gemv_rows_per_block(p[i].K);
-    g.blk0 = blocks;
-    blocks += (p[i].N + g.rows_pb - 1) / g.rows_pb;
-    if (p[i].K > maxK) maxK = p[i].K;
+    g.N = (int)p[i].N;
+    g.C = (int)(p[i].K / 64);
+    g.cfg = c.cfg;
+    g.CW = (g.C + c.S - 1) / c.S;
+    const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
+    const int groups = (g.N + c.RW - 1) / c.RW;
+    const int gpw = kGemvWaves / c.S;
+    int64_t n = (bytes * (int64_t)(cap - count) + total - 1) / total;
+    n = n < 1 ? 1 : n;
+    const int64_t most = (groups + gpw - 1) / gpw;
+    n = n > most ? most : n;
+    g.nwg = (int)n;
+    g.wg0 = wgs;
+    wgs += g.nwg;
+    if (c.S > 1) {  // one word per row group a workgroup visits
+      const int64_t steps = (groups + n * gpw - 1) / (n * gpw);
+      const int words = (int)(steps * gpw);
+      slots = words > slots ? words : slots;
+    }
   }
   a.count = count;
-  const size_t lds = (size_t)T * (maxK + 16);
-  dim3 grid((unsigned)blocks), block(kGemvThreads);
-  return T == 1 ? launch_gemv_t<1>(grid, block, lds, stream, a)
-                : launch_gemv_t<2>(grid, block, lds, stream, a);
+  a.slots = slots;
+  const size_t lds = sizeof(unsigned long long) * (size_t)slots;
+  if (big)
+    hipLaunchKernelGGL(gemv_kernel<2>, dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(gemv_kernel<1>, dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream, a);
+  return hipGetLastError();
 }

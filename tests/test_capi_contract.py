@@ -176,7 +176,8 @@ def test_forward_validation(lib):
     assert g(A, B, 1, 4096, C, D, 4096, MIS, None, None) == BL_ERR_ALIGN
     assert g(A, B, 1, 4096, C, D, 4096, E, MIS, None) == BL_ERR_ALIGN
     # explicit kernels outside their shapes
-    assert f(A, B, 3, 4096, C, D, 4096, E, None, 1, None) == BL_ERR_ARG  # gemv: T <= 2
+    assert f(A, B, 2, 4096, C, D, 4096, E, None, 1, None) == BL_ERR_ARG  # gemv: T == 1
+    assert f(A, B, 1, 4128, C, D, 4096, E, None, 1, None) == BL_ERR_ARG  # gemv: K % 64
     assert f(A, B, 1, 4160, C, D, 4096, E, None, 2, None) == BL_ERR_ARG  # skinny: K % 256
     assert f(A, B, 65, 4096, C, D, 4096, E, None, 2, None) == BL_ERR_ARG  # skinny: T <= 64
     assert f(A, B, 8, 4160, C, D, 4096, E, None, 3, None) == BL_ERR_ARG  # prefill: K % 128
@@ -189,6 +190,7 @@ def test_dispatch_choice(lib):
     f.restype = ctypes.c_int
     assert f(1, 4096, 4096) == 1
     assert f(1, 4096, 14336) == 1
+    assert f(2, 4096, 4096) == 2
     assert f(16, 4096, 4096) == 2
     assert f(64, 8192, 28672) == 2
     assert f(2048, 14336, 4096) == 3

@@ -115,7 +115,7 @@ bl_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
  * With BL_NO_NORM in flags, y = x (gain and eps are ignored).
  * Arguments:
  *   X        device fp32 [T, K], 16-byte aligned
- *   gain     device fp32 [K] or NULL (unit gain)
+ *   gain     device fp32 [K], 16-byte aligned, or NULL (unit gain)
  *   eps      finite, >= 0 (1e-6 in the Llama-shaped workloads)
  *   Xq       device int8 [T, K]; written
  *   x_scale  device fp32 [T]; receives s_t */
@@ -126,7 +126,7 @@ bl_status bitlinear_quantize_acts(const float* X, const float* gain, int64_t T, 
 /* One entry of a grouped activation quantization: all entries share T, eps, flags. */
 typedef struct bl_act_desc {
   const float* X;     /* device fp32 [T, K] */
-  const float* gain;  /* device fp32 [K] or NULL */
+  const float* gain;  /* device fp32 [K], 16-byte aligned, or NULL */
   int8_t* Xq;         /* device int8 [T, K] */
   float* x_scale;     /* device fp32 [T] */
   int64_t K;

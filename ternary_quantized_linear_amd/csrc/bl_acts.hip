@@ -36,49 +36,74 @@ struct ActArgs {
   int no_norm;
 };
 
-// Block-wide double-double sum. Each wave reduces its lanes with shuffles; after one
-// barrier every wave reduces the per-wave partials itself, in the same order, so all
-// waves hold the same bits without a second barrier.
+// Block-wide double-double sum. Each wave reduces its lanes with DPP into lane 63; after
+// one barrier every wave reduces the per-wave partials itself (DPP over the first NW
+// lanes, zeros beyond), in the same order, so all waves hold the same bits without a
+// second barrier.
 template <int NT>
 __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_hi,
                                              double* sh_lo) {
   constexpr int NW = NT / kWave;
+  static_assert(NW <= 16, "partials are combined within one DPP row");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    double oh = __shfl_xor(hi, m, kWave), ol = __shfl_xor(lo, m, kWave);
-    dd_add(hi, lo, oh, ol);
-  }
-  if (lane == 0) { sh_hi[wave] = hi; sh_lo[wave] = lo; }
+  group_dd_sum_to_last<kWave>(hi, lo);
+  if (lane == kWave - 1) { sh_hi[wave] = hi; sh_lo[wave] = lo; }
   __syncthreads();
   hi = lane < NW ? sh_hi[lane] : 0.0;
   lo = lane < NW ? sh_lo[lane] : 0.0;
-#pragma unroll
-  for (int m = NW / 2; m >= 1; m >>= 1) {
-    double oh = __shfl_xor(hi, m, kWave), ol = __shfl_xor(lo, m, kWave);
-    dd_add(hi, lo, oh, ol);
-  }
-  hi = __shfl(hi, 0, kWave);
-  lo = __shfl(lo, 0, kWave);
+  group_dd_sum_to_last<16>(hi, lo);
+  const double h = readlane_f64(hi, 15), l = readlane_f64(lo, 15);
+  hi = h;
+  lo = l;
 }
 
+// Block-wide maximum of non-negative values, same structure.
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* sh) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  v = wave_max_f32(v);
-  if (lane == 0) sh[wave] = v;
+  v = group_max_to_last<kWave>(v);
+  if (lane == kWave - 1) sh[wave] = v;
   __syncthreads();
   float m = lane < NW ? sh[lane] : 0.0f;
-#pragma unroll
-  for (int k = NW / 2; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, kWave));
-  return __shfl(m, 0, kWave);
+  m = group_max_to_last<16>(m);
+  return readlane_f32(m, 15);
 }
 
-__device__ __forceinline__ float norm_one(float x, double r, const float* gain, int k) {
+// Squares of fp32 values are exact in fp64. Four independent cascaded sums (one per
+// float4 component) keep four dependency chains in flight; they meet at the end.
+struct SumSq4 {
+  double h[4] = {0.0, 0.0, 0.0, 0.0}, l[4] = {0.0, 0.0, 0.0, 0.0};
+  __device__ __forceinline__ void add(float4 f) {
+    const double d[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dd_add1(h[c], l[c], d[c] * d[c]);
+  }
+  // one renormalized double-double pair
+  __device__ __forceinline__ void total(double& hi, double& lo) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const double s = h[c] + l[c];
+      l[c] = l[c] - (s - h[c]);
+      h[c] = s;
+    }
+    dd_add(h[0], l[0], h[1], l[1]);
+    dd_add(h[2], l[2], h[3], l[3]);
+    dd_add(h[0], l[0], h[2], l[2]);
+    hi = h[0];
+    lo = l[0];
+  }
+};
+
+__device__ __forceinline__ float norm_one(float x, double r, float g, bool has_gain) {
   double v = (double)x * r;
-  if (gain) v = v * (double)gain[k];
+  if (has_gain) v = v * (double)g;
   return (float)v;
+}
+
+__device__ __forceinline__ float4 norm4(float4 x, double r, float4 g, bool has_gain) {
+  return make_float4(norm_one(x.x, r, g.x, has_gain), norm_one(x.y, r, g.y, has_gain),
+                     norm_one(x.z, r, g.z, has_gain), norm_one(x.w, r, g.w, has_gain));
 }
 
 __device__ __forceinline__ uint32_t quant4(float4 y, float s) {
@@ -98,40 +123,27 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   const int t = blockIdx.x;
   const int K4 = e.K >> 2;
   const float4* x4 = reinterpret_cast<const float4*>(e.X + (int64_t)t * e.K);
-  float4 v[VPT];
+  const bool has_gain = e.gain != nullptr && !a.no_norm;
+  const float4* g4 = reinterpret_cast<const float4*>(e.gain);
+  // the row (and the gain) are loaded once, up front
+  float4 v[VPT], gv[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     int i = threadIdx.x + j * NT;
     v[j] = i < K4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    gv[j] = has_gain && i < K4 ? g4[i] : make_float4(1.f, 1.f, 1.f, 1.f);
   }
   if (!a.no_norm) {
-    double hi = 0.0, lo = 0.0;
+    SumSq4 acc;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      double d0 = v[j].x, d1 = v[j].y, d2 = v[j].z, d3 = v[j].w;
-      dd_add1(hi, lo, d0 * d0);
-      dd_add1(hi, lo, d1 * d1);
-      dd_add1(hi, lo, d2 * d2);
-      dd_add1(hi, lo, d3 * d3);
-    }
-    // renormalize the lane pair before the cross-lane adds
-    double s = hi + lo;
-    lo = lo - (s - hi);
-    hi = s;
+    for (int j = 0; j < VPT; ++j) acc.add(v[j]);
+    double hi, lo;
+    acc.total(hi, lo);
     block_dd_sum<NT>(hi, lo, sh_hi, sh_lo);
     const double ss = hi;  // hi + lo is already rounded into hi by dd_add
     const double r = 1.0 / sqrt(ss / (double)e.K + (double)a.eps);
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      int i = threadIdx.x + j * NT;
-      int k = 4 * i;
-      if (i < K4) {
-        v[j].x = norm_one(v[j].x, r, e.gain, k);
-        v[j].y = norm_one(v[j].y, r, e.gain, k + 1);
-        v[j].z = norm_one(v[j].z, r, e.gain, k + 2);
-        v[j].w = norm_one(v[j].w, r, e.gain, k + 3);
-      }
-    }
+    for (int j = 0; j < VPT; ++j) v[j] = norm4(v[j], r, gv[j], has_gain);
   }
   float m = 0.0f;
 #pragma unroll
@@ -157,29 +169,21 @@ __global__ __launch_bounds__(NT) void act_quant_stream(ActArgs a) {
   const int t = blockIdx.x;
   const int K4 = e.K >> 2;
   const float4* x4 = reinterpret_cast<const float4*>(e.X + (int64_t)t * e.K);
+  const bool has_gain = e.gain != nullptr && !a.no_norm;
+  const float4* g4 = reinterpret_cast<const float4*>(e.gain);
   double r = 1.0;
   if (!a.no_norm) {
-    double hi = 0.0, lo = 0.0;
-    for (int i = threadIdx.x; i < K4; i += NT) {
-      float4 f = x4[i];
-      double d0 = f.x, d1 = f.y, d2 = f.z, d3 = f.w;
-      dd_add1(hi, lo, d0 * d0);
-      dd_add1(hi, lo, d1 * d1);
-      dd_add1(hi, lo, d2 * d2);
-      dd_add1(hi, lo, d3 * d3);
-    }
-    double s = hi + lo;
-    lo = lo - (s - hi);
-    hi = s;
+    SumSq4 acc;
+    for (int i = threadIdx.x; i < K4; i += NT) acc.add(x4[i]);
+    double hi, lo;
+    acc.total(hi, lo);
     block_dd_sum<NT>(hi, lo, sh_hi, sh_lo);
     r = 1.0 / sqrt(hi / (double)e.K + (double)a.eps);
   }
   auto load_y = [&](int i) -> float4 {
-    float4 f = x4[i];
+    const float4 f = x4[i];
     if (a.no_norm) return f;
-    int k = 4 * i;
-    return make_float4(norm_one(f.x, r, e.gain, k), norm_one(f.y, r, e.gain, k + 1),
-                       norm_one(f.z, r, e.gain, k + 2), norm_one(f.w, r, e.gain, k + 3));
+    return norm4(f, r, has_gain ? g4[i] : make_float4(1.f, 1.f, 1.f, 1.f), has_gain);
   };
   float m = 0.0f;
   for (int i = threadIdx.x; i < K4; i += NT) {

@@ -30,7 +30,7 @@ bl_status check_acts(const float* X, const float* gain, int64_t T, int64_t K, in
   if (!X || !Xq || !xs) return BL_ERR_NULL;
   if (T <= 0 || K <= 0 || K % 4 || T > kMaxTokens) return BL_ERR_DIM;
   if (K > BL_MAX_K) return BL_ERR_K_TOO_LARGE;
-  if (!aligned16(X) || !aligned16(Xq) || !aligned_n(xs, 4) || (gain && !aligned_n(gain, 4)))
+  if (!aligned16(X) || !aligned16(Xq) || !aligned_n(xs, 4) || (gain && !aligned16(gain)))
     return BL_ERR_ALIGN;
   return BL_OK;
 }

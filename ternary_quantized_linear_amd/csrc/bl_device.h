@@ -33,6 +33,46 @@ __device__ __forceinline__ int group_sum_to_last(int v) {
   return v;
 }
 
+// The same moves for a double (both halves with one control) and a float. A lane whose
+// source is outside its row, or whose row is masked off, receives +0.0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xF, true);
+  const unsigned hi =
+      (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xF, true);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL, ROW_MASK>(__float_as_int(v)));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Maximum of non-negative v over each group of L lanes, into the group's last lane
+// (the +0.0 of lanes without a source never exceeds a non-negative value).
+template <int L>
+__device__ __forceinline__ float group_max_to_last(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x114>(v));
+  v = fmaxf(v, dpp_f32<0x118>(v));
+  if constexpr (L >= 32) v = fmaxf(v, dpp_f32<0x142, 0xA>(v));
+  if constexpr (L >= 64) v = fmaxf(v, dpp_f32<0x143, 0xC>(v));
+  return v;
+}
+
 __device__ __forceinline__ int wave_sum_i32(int v) {
   return __builtin_amdgcn_readlane(group_sum_to_last<64>(v), 63);
 }
@@ -73,6 +113,24 @@ __device__ __forceinline__ void dd_add(double& hi, double& lo, double bhi, doubl
   e += lo + blo;
   hi = s + e;               // fast-two-sum renormalization (|s| >= |e|)
   lo = e - (hi - s);
+}
+
+// Double-double sum over each group of L lanes into the group's last lane, in the same
+// DPP pattern as group_sum_to_last (a fixed order: every call combines the same pairs).
+template <int L>
+__device__ __forceinline__ void group_dd_sum_to_last(double& hi, double& lo) {
+#define BL_DD_STEP(...)                                              \
+  {                                                                  \
+    const double th = dpp_f64<__VA_ARGS__>(hi), tl = dpp_f64<__VA_ARGS__>(lo); \
+    dd_add(hi, lo, th, tl);                                          \
+  }
+  BL_DD_STEP(0xB1)
+  BL_DD_STEP(0x4E)
+  BL_DD_STEP(0x114)
+  BL_DD_STEP(0x118)
+  if constexpr (L >= 32) BL_DD_STEP(0x142, 0xA)
+  if constexpr (L >= 64) BL_DD_STEP(0x143, 0xC)
+#undef BL_DD_STEP
 }
 
 // Cascaded summation step: hi carries the rounded running sum, lo the sum of the

@@ -37,6 +37,8 @@
 #include "bl_device.h"
 #include "bl_internal.h"
 
+#include <climits>
+
 namespace bl {
 
 constexpr int kGemvThreads = 256;
@@ -58,6 +60,7 @@ struct GemvProj {
 };
 
 struct GemvArgs {
+  int wg0[BL_GROUP_CAP];  // first workgroup of each projection (one scalar load)
   GemvProj p[BL_GROUP_CAP];
   int count;
   int slots;  // 64-bit combine words per workgroup (0: no segmented rows)
@@ -145,14 +148,12 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   // lane chunk i is cbase + jl + L*i when that is inside the segment and the row; a
   // lane without a chunk reads its segment's first one (same cache line as lane 0)
   int ci[I];
-  uint4 x[I][4];
-  int xsum = 0;
+  bool on[I];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
     const int c = jl + L * i;
-    const bool on = c < cw && cbase + c < C;
-    ci[i] = on ? cbase + c : cbase;
-    load_act_chunk(P.Xq, ci[i], on, x[i], xsum);
+    on[i] = c < cw && cbase + c < C;
+    ci[i] = on[i] ? cbase + c : cbase;
   }
   const uint4* dummy = reinterpret_cast<const uint4*>(P.Xq);  // 64 bytes, L2-resident
   // the row group's base is wave-uniform (scalar); each lane adds a 32-bit offset
@@ -164,10 +165,18 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
 #pragma unroll
     for (int i = 0; i < I; ++i) w[i] = load_stream(base + (off < 0 ? (lane & 3) : off + ci[i]));
   };
+  // The weight ring goes out before the activations: vector loads complete in issue
+  // order, so this way the first row waits for one memory latency, not two in a row.
+  // The two scales come through the scalar cache, off the vector counter.
   uint4 w[kGemvDepth][I];
 #pragma unroll
   for (int d = 0; d < kGemvDepth; ++d) load_w(g0 + d * stride, w[d]);
-  const float f = P.ws[0] / P.xs[0];
+  uint4 x[I][4];
+  int xsum = 0;
+#pragma unroll
+  for (int i = 0; i < I; ++i) load_act_chunk(P.Xq, ci[i], on[i], x[i], xsum);
+  typedef const float __attribute__((address_space(4)))* ConstF;
+  const float f = *(ConstF)P.ws / *(ConstF)P.xs;
   int g = g0, k = 0;
   // one row group: consume buffer d, refill it D groups ahead (prefetch), write the row
   auto step = [&](int d, bool prefetch) {
@@ -214,11 +223,11 @@ template <int MAXI>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
   extern __shared__ unsigned long long slots[];
   const ArgsPtr a = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
-  const int count = a->count;
   const int wg = (int)blockIdx.x;
+  // wg0 ascends, unused entries hold INT_MAX: the projection is the count of starts <= wg
   int pi = 0;
-  for (int i = 1; i < count; ++i)
-    if (wg >= a->p[i].wg0) pi = i;
+#pragma unroll
+  for (int i = 1; i < BL_GROUP_CAP; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
   const GemvProj P = load_proj(a, pi);
   // the wave index is uniform per wave: readfirstlane keeps the row schedule, the
   // branches and the row bases in scalar registers
@@ -318,6 +327,7 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
     n = n > most ? most : n;
     g.nwg = (int)n;
     g.wg0 = wgs;
+    a.wg0[i] = wgs;
     wgs += g.nwg;
     if (c.S > 1) {  // one word per row group a workgroup visits
       const int64_t steps = (groups + n * gpw - 1) / (n * gpw);
@@ -325,6 +335,7 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
       slots = words > slots ? words : slots;
     }
   }
+  for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.slots = slots;
   const size_t lds = sizeof(unsigned long long) * (size_t)slots;

@@ -120,6 +120,7 @@ def test_quantize_acts_validation(lib):
     assert f(A, None, 8, 1024, 1e-6, 2, B, C, None) == BL_ERR_ARG
     assert f(MIS, None, 8, 1024, 1e-6, 0, B, C, None) == BL_ERR_ALIGN
     assert f(A, None, 8, 1024, 1e-6, 0, MIS, C, None) == BL_ERR_ALIGN
+    assert f(A, MIS, 8, 1024, 1e-6, 0, B, C, None) == BL_ERR_ALIGN  # gain
 
 
 class ActDesc(ctypes.Structure):

@@ -117,10 +117,13 @@ def test_quantize_acts_parity(bl, T, K, dist):
     assert_codes_equal(host(qg), q, X, "Xq")
 
 
-def test_quantize_acts_gain_noNorm_eps(bl):
-    X = workloads.acts_student_t(6, 2048, 3)
-    g = (1 + 0.3 * np.random.default_rng(1).standard_normal(2048)).astype(np.float32)
-    for kw in ({"gain": g}, {"flags": oracle.NO_NORM}, {"eps": 0.0}, {"eps": 0.5}):
+@pytest.mark.parametrize("T,K", [(6, 2048), (1, 14336), (2, 40000), (70, 4100), (65, 36000)])
+def test_quantize_acts_gain_noNorm_eps(bl, T, K):
+    # register-resident rows (few and many tokens) and the streaming variant
+    X = workloads.acts_student_t(T, K, 3)
+    g = (1 + 0.3 * np.random.default_rng(1).standard_normal(K)).astype(np.float32)
+    for kw in ({"gain": g}, {"flags": oracle.NO_NORM}, {"eps": 0.0}, {"eps": 0.5},
+               {"gain": g, "flags": oracle.NO_NORM}):
         q, s = oracle.quantize_acts(X, **kw)
         gk = dict(kw)
         if "gain" in gk:

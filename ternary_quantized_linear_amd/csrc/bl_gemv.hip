@@ -30,9 +30,10 @@
 //   - The wave index is made explicitly uniform (readfirstlane): the whole schedule stays
 //     in scalar registers and the row bases are scalar.
 //   - Unpacking is 5 ALU ops per packed dword: bit pairs 0, 1, 2 are masked in place
-//     (values u, 4u, 16u with u = q + 1 in {0, 1, 2}) and pair 3 shifted down, each into
-//     its own dot4 accumulator; the sum is a0 + a1/4 + a2/16 + a3 (exact shifts of exact
-//     multiples) started at minus the lane's own activation sum: sum x*q exactly.
+//     (values u, 4u, 16u with u = q + 1 in {0, 1, 2}) and pair 3 shifted down; pairs 0
+//     and 3 share one dot4 accumulator, pairs 1 and 2 have one each; the sum is
+//     a03 + a1/4 + a2/16 (exact shifts of exact multiples) started at minus the lane's
+//     own activation sum: sum x*q exactly.
 //   - Lane sums are reduced with DPP; Y = fp32(acc) * fp32(beta / s).
 #include "bl_device.h"
 #include "bl_internal.h"
@@ -43,7 +44,7 @@ namespace bl {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;  // 4
-constexpr int kGemvDepth = 4;                      // row groups in flight per wave
+constexpr int kGemvDepth = 2;                      // row groups in flight per wave
 constexpr int kGemvMaxC = 512;                     // K <= 32768
 
 struct GemvProj {
@@ -86,16 +87,16 @@ __device__ __forceinline__ GemvProj load_proj(ArgsPtr a, int i) {
   return P;
 }
 
-// Four accumulators, one per bit pair (pairs 1 and 2 carry factors 4 and 16).
+// Accumulators by factor: pairs 0 and 3 carry 1, pair 1 carries 4, pair 2 carries 16.
 struct Acc4 {
-  int a0, a1, a2, a3;
+  int a0, a1, a2;  // pairs 0 and 3 (factor 1) share a0
 };
 
 __device__ __forceinline__ void dot_word(uint32_t w, const uint4& x, Acc4& s) {
   s.a0 = sdot4(w & 0x03030303u, x.x, s.a0);
   s.a1 = sdot4(w & 0x0C0C0C0Cu, x.y, s.a1);
   s.a2 = sdot4(w & 0x30303030u, x.z, s.a2);
-  s.a3 = sdot4((w >> 6) & 0x03030303u, x.w, s.a3);
+  s.a0 = sdot4((w >> 6) & 0x03030303u, x.w, s.a0);
 }
 
 __device__ __forceinline__ void dot_chunk(const uint4 w, const uint4 (&x)[4], Acc4& s) {
@@ -106,7 +107,7 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, const uint4 (&x)[4], Ac
 }
 
 __device__ __forceinline__ int acc_total(const Acc4& s) {
-  return s.a0 + s.a3 + (s.a1 >> 2) + (s.a2 >> 4);
+  return s.a0 + (s.a1 >> 2) + (s.a2 >> 4);
 }
 
 // Activations of chunk c (64 codes): 4 x 16 bytes, transposed, and their sum; zeros when
@@ -157,13 +158,19 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   }
   const uint4* dummy = reinterpret_cast<const uint4*>(P.Xq);  // 64 bytes, L2-resident
   // the row group's base is wave-uniform (scalar); each lane adds a 32-bit offset
+  // (a scalar base plus a 32-bit unsigned byte offset per lane: one VGPR per address)
+  uint32_t boff[I];
+#pragma unroll
+  for (int i = 0; i < I; ++i) boff[i] = 16u * (uint32_t)ci[i];
+  const uint32_t doff = 16u * (uint32_t)(lane & 3);
   auto load_w = [&](int g, uint4 (&w)[I]) {
     const bool real = g <= glast;
     const int row0 = g * RW;
-    const uint4* base = real ? P.W + (int64_t)row0 * C : dummy;
-    const int off = real ? (min(row0 + sub, P.N - 1) - row0) * C : -1;
+    const char* base = reinterpret_cast<const char*>(real ? P.W + (int64_t)row0 * C : dummy);
+    const uint32_t roff = RW == 1 ? 0u : 16u * (uint32_t)((min(row0 + sub, P.N - 1) - row0) * C);
 #pragma unroll
-    for (int i = 0; i < I; ++i) w[i] = load_stream(base + (off < 0 ? (lane & 3) : off + ci[i]));
+    for (int i = 0; i < I; ++i)
+      w[i] = load_stream(reinterpret_cast<const uint4*>(base + (real ? roff + boff[i] : doff)));
   };
   // The weight ring goes out before the activations: vector loads complete in issue
   // order, so this way the first row waits for one memory latency, not two in a row.
@@ -178,30 +185,55 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   typedef const float __attribute__((address_space(4)))* ConstF;
   const float f = *(ConstF)P.ws / *(ConstF)P.xs;
   int g = g0, k = 0;
-  // one row group: consume buffer d, refill it D groups ahead (prefetch), write the row
+  // Row totals wait in a register (lane j holds slot j) and leave in one store per 64
+  // slots: no store sits between the ring's loads, so each wait counts loads only.
+  int res = 0;
+  unsigned long long keep = 0;  // bit j: slot j holds a row to write
+  int nb = 0, gb = g0;          // slots filled; row group of slot 0
+  auto flush = [&]() {
+    const int row = (gb + (lane / RW) * stride) * RW + lane % RW;
+    if (lane < nb && ((keep >> lane) & 1ull) && row < P.N) {
+      P.Y[row] = (float)res * f;
+      if (P.acc) P.acc[row] = res;
+    }
+    nb = 0;
+    keep = 0;
+    gb = g;
+  };
+  // one row group: consume buffer d, refill it D groups ahead (prefetch), keep the total
   auto step = [&](int d, bool prefetch) {
-    Acc4 s{-xsum, 0, 0, 0};
+    Acc4 s{-xsum, 0, 0};
 #pragma unroll
     for (int i = 0; i < I; ++i) dot_chunk(w[d][i], x[i], s);
     if (prefetch) load_w(g + kGemvDepth * stride, w[d]);
     int tot = group_sum_to_last<L>(acc_total(s));
-    const int row = g * RW + sub;
-    if ((lane & (L - 1)) == L - 1 && row < P.N) {
-      bool done = true;
-      if constexpr (S > 1) {
+    if constexpr (S > 1) {
+      // the S segment sums of this row meet in one LDS word; the wave that completes
+      // the count holds the row total
+      int done = 0;
+      if (lane == kWave - 1) {
         const unsigned long long mine = (1ull << 40) + (unsigned long long)(long long)tot;
         const unsigned long long now = atomicAdd(&slots[k * GPW + wave / S], mine) + mine;
         const unsigned long long n = (now + (1ull << 39)) >> 40;
         done = n == (unsigned long long)S;
         tot = (int)(long long)(now - (n << 40));
       }
-      if (done) {
-        P.Y[row] = (float)tot * f;
-        if (P.acc) P.acc[row] = tot;
+      const int t = __builtin_amdgcn_readlane(tot, kWave - 1);
+      res = lane == nb ? t : res;
+      keep |= (unsigned long long)(__builtin_amdgcn_readlane(done, kWave - 1) & 1) << nb;
+      nb += 1;
+    } else {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int t = __builtin_amdgcn_readlane(tot, r * L + L - 1);
+        res = lane == nb + r ? t : res;
       }
+      keep |= ((1ull << RW) - 1) << nb;
+      nb += RW;
     }
     g += stride;
     ++k;
+    if (nb == kWave) flush();
   };
   // Whole rounds of D groups in a loop with a single exit, then the remaining groups
   // (already in flight) straight-line: no exit in the middle of the ring, so the wait
@@ -215,6 +247,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
 #pragma unroll
   for (int d = 0; d < kGemvDepth - 1; ++d)
     if (d < left) step(d, false);
+  flush();
 }
 
 // MAXI = 2 adds the mapping for rows of more than 256 chunks (two chunks per lane);
@@ -289,24 +322,44 @@ using namespace bl;
 
 bool bl_gemv_supports(int T, int K) { return T == 1 && K % 64 == 0 && K / 64 <= kGemvMaxC; }
 
+// Relative cost of a byte streamed by segmented rows (S waves meet per row in LDS and
+// an eighth of a segment's lanes may idle) against a byte of a one-wave row, in 1/16.
+#ifndef BL_GEMV_SEG_COST16
+#define BL_GEMV_SEG_COST16 20
+#endif
+
 hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
   (void)T;
   GemvArgs a{};
   int64_t total = 0;
   GemvCfg cfg[BL_GROUP_CAP];
+  int64_t cost[BL_GROUP_CAP];
+  int order[BL_GROUP_CAP];
   bool big = false;
   for (int i = 0; i < count; ++i) {
     cfg[i] = gemv_cfg((int)(p[i].K / 64));
     big = big || cfg[i].cfg == 5;
-    total += (int64_t)p[i].N * (p[i].K / 4);
+    const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
+    cost[i] = cfg[i].S > 1 ? bytes * BL_GEMV_SEG_COST16 / 16 : bytes;
+    total += cost[i];
+    order[i] = i;
   }
+  // Costliest partitions first: workgroups are dispatched in index order over about a
+  // microsecond, and the partition that needs the most time should not start last.
+  for (int i = 1; i < count; ++i)
+    for (int j = i; j > 0 && cost[order[j]] > cost[order[j - 1]]; --j) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
   // One round of resident workgroups (the combine words take at most a few KB of LDS);
-  // each projection gets workgroups in proportion to its bytes, at least one and never
+  // each projection gets workgroups in proportion to its cost, at least one and never
   // one without a row group.
   const int cap = gemv_resident(big, 4096);
   int wgs = 0, slots = 0;
-  for (int i = 0; i < count; ++i) {
-    GemvProj& g = a.p[i];
+  for (int o = 0; o < count; ++o) {
+    const int i = order[o];
+    GemvProj& g = a.p[o];
     const GemvCfg c = cfg[i];
     g.Xq = p[i].Xq;
     g.xs = p[i].x_scale;
@@ -318,16 +371,15 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
     g.C = (int)(p[i].K / 64);
     g.cfg = c.cfg;
     g.CW = (g.C + c.S - 1) / c.S;
-    const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
     const int groups = (g.N + c.RW - 1) / c.RW;
     const int gpw = kGemvWaves / c.S;
-    int64_t n = (bytes * (int64_t)(cap - count) + total - 1) / total;
+    int64_t n = (cost[i] * (int64_t)(cap - count) + total - 1) / total;
     n = n < 1 ? 1 : n;
     const int64_t most = (groups + gpw - 1) / gpw;
     n = n > most ? most : n;
     g.nwg = (int)n;
     g.wg0 = wgs;
-    a.wg0[i] = wgs;
+    a.wg0[o] = wgs;
     wgs += g.nwg;
     if (c.S > 1) {  // one word per row group a workgroup visits
       const int64_t steps = (groups + n * gpw - 1) / (n * gpw);

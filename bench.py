@@ -41,7 +41,28 @@ def parse():
     ap.add_argument("--only-decode", action="store_true", help="skip the extra workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy kernel (counter calibration)")
+    ap.add_argument("--counter-pass", type=int, default=0, metavar="N",
+                    help="hardware-counter pass: N eager decode steps and the calibration "
+                         "copy, no graphs and no JSON line (for rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- HBM traffic counters
+
+def counted_traffic():
+    """HBM bytes per grouped GEMV launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE passes scaled by a copy kernel of known size), or None when the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "gemv_kernel_decode8b_counters.json")
+    try:
+        rec = json.load(open(rec_path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("traffic_bytes_per_dispatch")
 
 
 # ---------------------------------------------------------------- timing helpers
@@ -363,6 +384,16 @@ def main():
         sys.exit(2)
     T = 1
     d = setup_decode(torch, bl, workloads, T)
+    if a.counter_pass > 0:
+        # eager launches only: each dispatch is counted on its own
+        for i in range(a.counter_pass):
+            d["qa"]()
+            d["fws"][i % len(d["fws"])]()
+        torch.cuda.synchronize()
+        run_calib_copy(torch)
+        print("counter pass: %d decode steps and the 256 MiB copy done" % a.counter_pass,
+              flush=True)
+        return
     r = run_decode(torch, d, a.steps, a.warmup)
     step_bytes = d["gemv_bytes"] + d["act_bytes"]
     value = step_bytes / (r["ms_step"] * 1e-3) / 1e9
@@ -389,7 +420,7 @@ def main():
                    "bytes_per_step": step_bytes, "frac_hbm_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1> (grouped, 7 projections)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
                      "bytes_per_launch": d["gemv_bytes"],
                      "avg_launch_us": round(r["ms_gemv"] * 1e3, 3)},
         "act_quant": {"avg_launch_us": round(r["ms_act"] * 1e3, 3),

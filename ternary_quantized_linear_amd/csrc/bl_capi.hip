@@ -48,10 +48,11 @@ bl_status check_proj(const int8_t* Xq, const float* xs, int64_t T, int64_t K,
 
 bl_kernel choose(int64_t T, int64_t N, int64_t K) {
   (void)N;
-  if (bl_gemv_supports((int)T, (int)K) && T <= 2) return BL_KERNEL_GEMV;
-  if (T <= 64 && bl_skinny_supports((int)T, (int)K)) return BL_KERNEL_SKINNY;
-  if (T > 64 && bl_prefill_supports((int)T, (int)K)) return BL_KERNEL_PREFILL;
+  // one token: dot4 GEMV; up to 32 tokens: the streaming MFMA kernel; beyond, the
+  // LDS-tiled MFMA GEMM
   if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
+  if (bl_skinny_supports((int)T, (int)K)) return BL_KERNEL_SKINNY;
+  if (bl_prefill_supports((int)T, (int)K)) return BL_KERNEL_PREFILL;
   return BL_KERNEL_GENERIC;
 }
 

@@ -1,4 +1,4 @@
-// bl_skinny.hip -- ternary x int8 product for 1 < T <= 64 tokens on int8 MFMA
+// bl_skinny.hip -- ternary x int8 product for 1 < T <= 32 tokens on int8 MFMA
 // (v_mfma_i32_16x16x64_i8), int32 accumulation, fused rescale.
 //
 // [HF-1.58] "Fine-tuning LLMs to 1.58 bits", "Inference optimization and custom
@@ -6,25 +6,34 @@
 // "Computation paradigm": integer arithmetic only. [bitnet.cpp] "3. BitLinear
 // operation": rescale by the weight and activation scales.
 //
-// Below ~80 tokens the product is bound by the packed-weight stream (2 ops per weight per
-// token against 1/4 byte per weight), so the kernel is built like the decode GEMV: every
-// weight byte is read from HBM once, straight into registers, by waves that each keep a
-// ring of loads in flight, with no barrier in the main loop.
-//   - A row group is 16*RB weight rows (RB MFMA row blocks). A row group's K is cut into
-//     S = 1, 2 or 4 contiguous segments of 256-code chunks, one per wave of the
-//     workgroup; the S partial tiles meet in LDS (atomic adds and an arrival count; the
-//     last wave writes the tile).
-//   - Per chunk a lane loads 16 bytes of row (lane % 16) of each row block, codes
-//     64*(lane/16) .. +63: one 128-bit load feeds four MFMAs, whose A operands are the
-//     u = q + 1 codes of one dword each (unpack_u2, p-major order). The B operands are
-//     the matching 16 activation bytes of token (lane % 16) + 16*tb, loaded from global
-//     memory (L2) with the weights and 4x4 byte-transposed to the same order; tokens past
-//     T reuse the last token's bytes and their output columns are dropped.
-//   - sum x*u - sum x = sum x*q: the sum of the activations comes from one more MFMA per
-//     B operand with an all-ones A, so the VALU only unpacks and transposes.
+// With few tokens the product is bound by the packed-weight stream (2 ops per weight per
+// token against 1/4 byte per weight): every weight byte is read from HBM once, straight
+// into registers, by waves that keep a ring of loads in flight.
+//   - A workgroup has 8 waves: S teams (S = 1, 2 or 4) of G = 8/S waves. Team s owns
+//     the s-th of S contiguous K segments; its G waves own G row blocks of 16 rows. A
+//     step is 512 codes: per row block a lane loads 32 bytes (row lane % 16, bytes
+//     32*(lane/16) of the step's 128) with two 128-bit loads, so every instruction pair
+//     reads whole 128-byte lines, and feeds eight MFMAs.
+//   - The activations of a step (16*TB tokens x 512 codes per team) are loaded once per
+//     workgroup, coalesced, by all 512 threads, each step's ahead of its weights (so
+//     that waiting for them never waits for those weights),
+//     4x4 byte-transposed to the unpack order and written to one of two LDS stages, laid
+//     out so that each MFMA's B operand is one conflict-free 1 KB read. One barrier per
+//     step hands a stage from writers to readers; the weight loads in flight are not
+//     waited for there.
+//   - MFMA j of a step takes codes 64j + 16*ks for lane k-slot ks: each token's four
+//     lanes read 64 contiguous staged bytes. The A operand of MFMA j at lane (row, ks) is
+//     the packed dword at byte 16j + 4ks of the row's 128 bytes, which lane (row, j / 2)
+//     loaded as its register 4*(j % 2) + ks: two 4x4 transposes across the four lane
+//     rows (v_permlane32_swap, v_permlane16_swap) bring them over, and unpack_u2 gives
+//     u = q + 1 in p-major order.
+//   - sum x*u - sum x = sum x*q: the activation sum comes from one more MFMA per B
+//     operand with an all-ones A operand.
+//   - The S teams' partial tiles meet in LDS at the end of each row-block iteration;
+//     team 0 rescales and stores Y = fp32(acc) * fp32(beta / s_t).
 //   - Workgroups are partitioned among the projections of a grouped call in proportion
 //     to their bytes; the grid is one round of resident workgroups.
-// Output tile: MFMA lane l, register r holds row 4*(l/16) + r of the block, token l % 16.
+// MFMA output: lane l, register r holds row 4*(l/16) + r of the block, token l % 16.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -34,11 +43,13 @@ namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kSkThreads = 256;
-constexpr int kSkWaves = kSkThreads / kWave;  // 4
-constexpr int kSkDepth = 2;                    // chunks in flight per wave
-constexpr int kSkRB = 2;                       // MFMA row blocks per row group
-constexpr size_t kSkLdsMax = 64 * 1024;
+constexpr int kSkWaves = 8;
+constexpr int kSkThreads = kSkWaves * kWave;  // 512
+constexpr int kSkDepth = 2;                    // steps in flight (weights and activations)
+constexpr int kSkKS = 512;                     // codes per step
+constexpr int kSkNM = kSkKS / 64;              // MFMAs per step per token block
+constexpr int kSkStepBytes = kSkKS / 4;        // packed bytes per row per step
+constexpr size_t kSkLdsMax = 80 * 1024;        // two workgroups per CU
 
 struct SkProj {
   const int8_t* Xq;
@@ -47,10 +58,10 @@ struct SkProj {
   const float* ws;
   float* Y;
   int32_t* acc;
-  int N, K, C4;   // C4 = 256-code chunks per row
-  int wg0, nwg;   // this projection's workgroups
-  int S, CW;      // K segments per row group, chunks per segment
-  int tile;       // LDS words of one combine tile (S > 1)
+  int N, K;
+  int steps;    // ceil(K / 512)
+  int wg0, nwg;
+  int S, CW;    // teams (K segments) and steps per segment
 };
 
 struct SkArgs {
@@ -58,7 +69,6 @@ struct SkArgs {
   SkProj p[BL_GROUP_CAP];
   int count;
   int T;
-  int lds_words;  // combine words per workgroup (0: no segmented row groups)
 };
 
 typedef const SkArgs __attribute__((address_space(4)))* SkArgsPtr;
@@ -73,203 +83,223 @@ __device__ __forceinline__ SkProj load_sk(SkArgsPtr a, int i) {
   P.acc = a->p[i].acc;
   P.N = a->p[i].N;
   P.K = a->p[i].K;
-  P.C4 = a->p[i].C4;
+  P.steps = a->p[i].steps;
   P.wg0 = a->p[i].wg0;
   P.nwg = a->p[i].nwg;
   P.S = a->p[i].S;
   P.CW = a->p[i].CW;
-  P.tile = a->p[i].tile;
   return P;
 }
 
-__device__ __forceinline__ v4i as_v4i(const uint4& v) {
-  return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+// 4x4 transpose of dwords across the four 16-lane rows: on return, register q of lane
+// (row s) holds what register s of lane (row q) held.
+__device__ __forceinline__ void transpose_rows(uint32_t (&r)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r[0] = c[0];
+  r[1] = c[1];
+  r[2] = d[0];
+  r[3] = d[1];
 }
 
-__device__ __forceinline__ v4i transpose_v4i(const uint4& v) {
-  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-  transpose16(in, o);
-  return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+// LDS bytes of one stage and of a whole workgroup, per team count S and token blocks TB.
+__host__ __device__ constexpr int sk_stage_bytes(int S, int TB) { return S * kSkNM * TB * 1024; }
+__host__ __device__ constexpr int sk_lds_bytes(int S, int TB) {
+  return 2 * sk_stage_bytes(S, TB) + kSkWaves * TB * 1024;
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int d) {
-  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
-}
-
-// One projection's partition: row groups g = wgl * (4/S) + wave / S + it * stride, wave
-// wave % S taking K segment wave % S of each.
 template <int TB, int S>
-__device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wave, int* lds) {
-  constexpr int RB = kSkRB;
-  constexpr int GPW = kSkWaves / S;  // row groups per workgroup step
+__device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wave, uint8_t* lds) {
+  constexpr int G = kSkWaves / S;
   constexpr int D = kSkDepth;
-  const int lane = threadIdx.x & (kWave - 1), li = lane & 15, lg = lane >> 4;
-  const int nrg = (P.N + 16 * RB - 1) / (16 * RB);
-  const int stride = P.nwg * GPW;
-  const int grp = wave / S;
-  const int g0 = wgl * GPW + grp;
-  if (g0 >= nrg) return;  // the S waves of a row group leave together
-  const int niter = (nrg - 1 - g0) / stride + 1;
-  const int c0 = (wave % S) * P.CW;
-  const int nck = min(P.C4, c0 + P.CW) - c0;
+  constexpr int PIECES = S * 16 * TB * (kSkKS / 16);  // 16-byte activation pieces per step
+  constexpr int PPT = (PIECES + kSkThreads - 1) / kSkThreads;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), li = lane & 15, lg = lane >> 4;
+  const int seg = wave / G, mem = wave % G;
+  const int nrb = (P.N + 15) / 16;
+  // every wave of the workgroup runs the same number of steps (one barrier per step)
+  const int niter = (nrb - wgl * G + P.nwg * G - 1) / (P.nwg * G);
+  const int CW = P.CW;
+  const int total = niter * CW;
   const int Kb = P.K >> 2;
-  const int total = niter * nck;
+  uint8_t* stage0 = lds;
+  uint8_t* stage1 = lds + sk_stage_bytes(S, TB);
+  int* comb = reinterpret_cast<int*>(lds + 2 * sk_stage_bytes(S, TB));
 
-  // per-lane constant parts of the addresses
-  uint32_t xoff[TB];
-  float fac[TB];
-  typedef const float __attribute__((address_space(4)))* ConstF;
-  const float beta = *(ConstF)P.ws;
+  // activation pieces this thread stages: piece q = tid + p * 512 -> team, token, offset
+  int pt_tok[PPT], pt_seg[PPT], pt_off[PPT], pt_lds[PPT];
+  bool pt_on[PPT];
+#pragma unroll
+  for (int p = 0; p < PPT; ++p) {
+    const int q = tid + p * kSkThreads;
+    pt_on[p] = q < PIECES;
+    const int qq = pt_on[p] ? q : 0;
+    const int o16 = qq % (kSkKS / 16);
+    const int t = (qq / (kSkKS / 16)) % (16 * TB);
+    const int s = qq / ((kSkKS / 16) * 16 * TB);
+    pt_tok[p] = min(t, T - 1);  // tokens past T: any valid row (their columns are dropped)
+    pt_seg[p] = s;
+    pt_off[p] = 16 * o16;
+    const int j = o16 >> 2, ks = o16 & 3;
+    pt_lds[p] = ((((s * kSkNM + j) * TB + (t >> 4)) * kWave) + ks * 16 + (t & 15)) * 16;
+  }
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(P.Xq);
+
+  uint4 w[D][2];
+  uint4 xr[D][PPT];
+  // weights of step n (iteration n / CW, segment step n % CW) into ring slot d: this
+  // wave's row block, its team's segment; lanes past the row end read a dummy block
+  auto load_w = [&](int n, int d) {
+    const int it = n / CW, m = n - it * CW;
+    const int rb = (wgl + it * P.nwg) * G + mem;
+    const int st = seg * CW + m;
+    const bool real = n < total && st * kSkKS + 128 * lg < P.K;
+    const int row = min(rb * 16 + li, P.N - 1);
+    const uint8_t* wp =
+        real ? P.W + (int64_t)row * Kb + st * kSkStepBytes + 32 * lg : dummy + 32 * (lane & 3);
+    w[d][0] = *reinterpret_cast<const uint4*>(wp);
+    w[d][1] = *reinterpret_cast<const uint4*>(wp + 16);
+  };
+  // activations of step n into slot d: pieces of every team's step (past the row end,
+  // any valid bytes: they are replaced by zeros when staged)
+  auto load_x = [&](int n, int d) {
+    const int m = n - (n / CW) * CW;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      if (!pt_on[p]) continue;  // wave-uniform: pieces come in whole waves
+      const int code = min((pt_seg[p] * CW + m) * kSkKS + pt_off[p], P.K - 16);
+      xr[d][p] = *reinterpret_cast<const uint4*>(P.Xq + (int64_t)pt_tok[p] * P.K + code);
+    }
+  };
+  // staged activations of step n (from slot d), transposed; zero past the row end
+  auto stage = [&](int n, int d, uint8_t* dst) {
+    const int m = n - (n / CW) * CW;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      if (!pt_on[p]) continue;
+      uint4 v = xr[d][p];
+      if ((pt_seg[p] * CW + m) * kSkKS + pt_off[p] >= P.K) v = make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+      transpose16(in, o);
+      *reinterpret_cast<uint4*>(dst + pt_lds[p]) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  v4i acc[TB], cs[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
-    const int t = min(16 * tb + li, T - 1);
-    xoff[tb] = (uint32_t)t * (uint32_t)P.K + 64u * (uint32_t)lg;
-    fac[tb] = beta / P.xs[t];
+    acc[tb] = v4i{0, 0, 0, 0};
+    cs[tb] = v4i{0, 0, 0, 0};
   }
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(P.Xq);  // 64 L2-resident bytes
-  const uint32_t doff = 16u * (uint32_t)(lane & 3);
+  typedef const float __attribute__((address_space(4)))* ConstF;
+  const float beta = *(ConstF)P.ws;
+  float fac[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) fac[tb] = beta / P.xs[min(16 * tb + li, T - 1)];
 
-  uint4 w[D][RB];
-  uint4 b[D][TB][4];
-  auto load = [&](int it, int m, int d) {
-    const bool real = it < niter;
-    const int row0 = (g0 + it * stride) * 16 * RB;
-    const int chunk = c0 + min(m, nck - 1);
-    const uint8_t* wbase = real ? P.W + (int64_t)row0 * Kb : dummy;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint32_t roff =
-          (uint32_t)(min(row0 + rb * 16 + li, P.N - 1) - row0) * (uint32_t)Kb + 64u * chunk + 16u * lg;
-      w[d][rb] = load_stream(reinterpret_cast<const uint4*>(wbase + (real ? roff : doff)));
-    }
-    const uint8_t* xbase = reinterpret_cast<const uint8_t*>(P.Xq) + 256 * chunk;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        b[d][tb][q] = *reinterpret_cast<const uint4*>(xbase + xoff[tb] + 16 * q);
-  };
-
-  v4i acc[RB][TB], cs[TB];
-  auto clear = [&]() {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      cs[tb] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb][tb] = v4i{0, 0, 0, 0};
-    }
-  };
-  clear();
-
-  // row group finished by this wave: combine the S segments, rescale, store
+  // end of a row-block iteration: teams meet in LDS, team 0 stores
   auto finish = [&](int it) {
-    const int row0 = (g0 + it * stride) * 16 * RB;
-    v4i res[RB][TB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) res[rb][tb] = acc[rb][tb] - cs[tb];
-    bool last = true;
     if constexpr (S > 1) {
-      int* tile = lds + (it * GPW + grp) * P.tile;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            atomicAdd(&tile[((rb * TB + tb) * 4 + r) * kWave + lane], res[rb][tb][r]);
-      int arrived = 0;
-      if (lane == 0) arrived = atomicAdd(&tile[RB * TB * 4 * kWave], 1);
-      last = __builtin_amdgcn_readfirstlane(arrived) == S - 1;
-      if (last) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              res[rb][tb][r] = atomicAdd(&tile[((rb * TB + tb) * 4 + r) * kWave + lane], 0);
-      }
+        for (int r = 0; r < 4; ++r)
+          comb[(((seg * G + mem) * TB + tb) * 4 + r) * kWave + lane] = acc[tb][r] - cs[tb][r];
+      __syncthreads();
     }
-    if (last) {
+    if (seg == 0) {
+      const int row0 = ((wgl + it * P.nwg) * G + mem) * 16;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
+        v4i v = acc[tb] - cs[tb];
+#pragma unroll
+        for (int s2 = 1; s2 < S; ++s2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += comb[(((s2 * G + mem) * TB + tb) * 4 + r) * kWave + lane];
         const int tok = 16 * tb + li;
         if (tok < T) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = row0 + rb * 16 + 4 * lg + r;
-              if (row < P.N) {
-                const int v = res[rb][tb][r];
-                P.Y[(int64_t)tok * P.N + row] = (float)v * fac[tb];
-                if (P.acc) P.acc[(int64_t)tok * P.N + row] = v;
-              }
+          for (int r = 0; r < 4; ++r) {
+            const int row = row0 + 4 * lg + r;
+            if (row < P.N) {
+              P.Y[(int64_t)tok * P.N + row] = (float)v[r] * fac[tb];
+              if (P.acc) P.acc[(int64_t)tok * P.N + row] = v[r];
             }
+          }
         }
       }
     }
-    clear();
-  };
-
-  int itp = 0, mp = 0;  // next chunk to load
-  auto advance = [&](int& it, int& m) {
-    if (++m == nck) {
-      m = 0;
-      ++it;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      acc[tb] = v4i{0, 0, 0, 0};
+      cs[tb] = v4i{0, 0, 0, 0};
     }
   };
+
+  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  // prologue: steps 0 and 1 in flight, each step's activations ahead of its weights
+  // (waiting for the activations of a step never waits for its weights); step 0 staged
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    load(itp, mp, d);
-    advance(itp, mp);
+    load_x(d, d);
+    load_w(d, d);
   }
-  int itc = 0, mc = 0;  // next chunk to consume
-  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  auto step = [&](int d, bool prefetch) {
+  stage(0, 0, stage0);
+  __syncthreads();
+
+  // step n consumes ring slot and stage n % 2, issues step n + 2 into that slot and
+  // stages step n + 1 from the other one
+  auto step = [&](int n, int d, bool prefetch) {
+    uint8_t* cur = d ? stage1 : stage0;
+    uint8_t* nxt = d ? stage0 : stage1;
+    // A operands: MFMA j's dword ks sits in lane row j / 2, register 4 * (j % 2) + ks
+    uint32_t a0[4] = {w[d][0].x, w[d][0].y, w[d][0].z, w[d][0].w};
+    uint32_t a1[4] = {w[d][1].x, w[d][1].y, w[d][1].z, w[d][1].w};
+    transpose_rows(a0);
+    transpose_rows(a1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v4i bt[TB];
+    for (int j = 0; j < kSkNM; ++j) {
+      uint32_t u[4];
+      unpack_u2((j & 1) ? a1[j >> 1] : a0[j >> 1], u);
+      const v4i ua = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        bt[tb] = transpose_v4i(b[d][tb][q]);
-        cs[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, bt[tb], cs[tb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        uint32_t u[4];
-        unpack_u2(word_of(w[d][rb], q), u);
-        const v4i ua = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-          acc[rb][tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, bt[tb], acc[rb][tb], 0, 0, 0);
+        const uint4 bx = *reinterpret_cast<const uint4*>(
+            cur + (((seg * kSkNM + j) * TB + tb) * kWave + lane) * 16);
+        const v4i bv = v4i{(int)bx.x, (int)bx.y, (int)bx.z, (int)bx.w};
+        acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, bv, acc[tb], 0, 0, 0);
+        cs[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, bv, cs[tb], 0, 0, 0);
       }
     }
     if (prefetch) {
-      load(itp, mp, d);
-      advance(itp, mp);
+      load_x(n + D, d);
+      load_w(n + D, d);
     }
-    if (mc == nck - 1) finish(itc);
-    advance(itc, mc);
+    if (n + 1 < total) stage(n + 1, d ^ 1, nxt);
+    const int it = n / CW;
+    if (n - it * CW == CW - 1) finish(it);
+    __syncthreads();
   };
-  // whole rounds of D chunks in a loop with one exit, then the rest straight-line
-  int left = total;
-  while (left >= D) {
+  // whole rounds of D steps, then the rest: every wave of the workgroup runs the same
+  // steps, so every barrier is reached by all of them
+  int n = 0;
+  while (total - n >= D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) step(d, true);
-    left -= D;
+    for (int d = 0; d < D; ++d) step(n + d, d, true);
+    n += D;
   }
 #pragma unroll
   for (int d = 0; d < D - 1; ++d)
-    if (d < left) step(d, false);
+    if (n + d < total) step(n + d, d, false);
 }
 
 template <int TB>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
-  extern __shared__ int sk_lds[];
+  extern __shared__ uint4 sk_lds[];
   const SkArgsPtr a = (SkArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
   const int wg = (int)blockIdx.x;
   int pi = 0;
@@ -279,14 +309,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   const int T = a->T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wgl = wg - P.wg0;
-  if (P.S > 1) {  // combine tiles start at zero
-    for (int i = threadIdx.x; i < a->lds_words; i += kSkThreads) sk_lds[i] = 0;
-    __syncthreads();
-  }
+  uint8_t* lds = reinterpret_cast<uint8_t*>(sk_lds);
   switch (P.S) {
-    case 1: sk_sweep<TB, 1>(P, T, wgl, wave, sk_lds); break;
-    case 2: sk_sweep<TB, 2>(P, T, wgl, wave, sk_lds); break;
-    default: sk_sweep<TB, 4>(P, T, wgl, wave, sk_lds); break;
+    case 1: sk_sweep<TB, 1>(P, T, wgl, wave, lds); break;
+    case 2: sk_sweep<TB, 2>(P, T, wgl, wave, lds); break;
+    default:
+      if constexpr (TB == 1) sk_sweep<TB, 4>(P, T, wgl, wave, lds);
+      break;
   }
 }
 
@@ -307,6 +336,15 @@ int sk_resident(size_t lds) {
   return cus * per;
 }
 
+// Teams per row block: segments of at least 4 steps, more teams while the row blocks
+// alone would leave the device short of waves.
+int sk_teams(int steps, int nrb, int TB) {
+  const int smax = TB == 1 ? 4 : 2;  // keeps the stages and the combine area within 80 KB
+  int S = 1;
+  while (S < smax && steps / (2 * S) >= 4 && nrb * S < 4096) S *= 2;
+  return S;
+}
+
 // The dynamic-LDS limit is raised once per instance (first launch), never inside a
 // stream capture after that.
 template <int TB>
@@ -316,60 +354,45 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
   if (attr != hipSuccess) return attr;
   SkArgs a{};
   int64_t total = 0;
-  for (int i = 0; i < count; ++i) total += (int64_t)p[i].N * (p[i].K / 4);
-  // S: enough chunks per segment (at least 8) to keep the ring busy
-  int S[BL_GROUP_CAP];
+  size_t lds = 0;
   for (int i = 0; i < count; ++i) {
-    const int c4 = p[i].K / 256;
-    S[i] = c4 >= 32 ? 4 : c4 >= 16 ? 2 : 1;
+    SkProj& s = a.p[i];
+    s.Xq = p[i].Xq;
+    s.xs = p[i].x_scale;
+    s.W = p[i].W;
+    s.ws = p[i].w_scale;
+    s.Y = p[i].Y;
+    s.acc = p[i].acc;
+    s.N = p[i].N;
+    s.K = p[i].K;
+    s.steps = (p[i].K + kSkKS - 1) / kSkKS;
+    s.S = sk_teams(s.steps, (s.N + 15) / 16, TB);
+    s.CW = (s.steps + s.S - 1) / s.S;
+    const size_t need = (size_t)sk_lds_bytes(s.S, TB);
+    lds = need > lds ? need : lds;
+    total += (int64_t)p[i].N * (p[i].K / 4);
   }
-  const int tile = kSkRB * TB * 4 * kWave + 4;  // partial sums + arrival count (padded)
-  int cap = 0;
-  int wgs = 0, words = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    // first pass: partition with the occupancy at the LDS the partition needs
-    cap = sk_resident<TB>(sizeof(int) * (size_t)words);
-    wgs = 0;
-    words = 0;
-    for (int i = 0; i < count; ++i) {
-      SkProj& s = a.p[i];
-      s.Xq = p[i].Xq;
-      s.xs = p[i].x_scale;
-      s.W = p[i].W;
-      s.ws = p[i].w_scale;
-      s.Y = p[i].Y;
-      s.acc = p[i].acc;
-      s.N = p[i].N;
-      s.K = p[i].K;
-      s.C4 = p[i].K / 256;
-      s.S = S[i];
-      s.CW = (s.C4 + s.S - 1) / s.S;
-      s.tile = tile;
-      const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
-      const int nrg = (p[i].N + 16 * kSkRB - 1) / (16 * kSkRB);
-      const int gpw = kSkWaves / s.S;
-      int64_t n = (bytes * (int64_t)(cap - count) + total - 1) / total;
-      n = n < 1 ? 1 : n;
-      const int64_t most = (nrg + gpw - 1) / gpw;
-      n = n > most ? most : n;
-      s.nwg = (int)n;
-      s.wg0 = wgs;
-      a.wg0[i] = wgs;
-      wgs += s.nwg;
-      if (s.S > 1) {
-        const int64_t iters = (nrg + n * gpw - 1) / (n * gpw);
-        const int64_t need = iters * gpw * tile;
-        if (need > words) words = (int)need;
-      }
-    }
+  if (lds > kSkLdsMax) return hipErrorInvalidValue;
+  const int cap = sk_resident<TB>(lds);
+  int wgs = 0;
+  for (int i = 0; i < count; ++i) {
+    SkProj& s = a.p[i];
+    const int G = kSkWaves / s.S;
+    const int nrb = (s.N + 15) / 16;
+    const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
+    int64_t n = (bytes * (int64_t)(cap - count) + total - 1) / total;
+    n = n < 1 ? 1 : n;
+    const int64_t most = (nrb + G - 1) / G;  // no workgroup without a row block
+    n = n > most ? most : n;
+    s.nwg = (int)n;
+    s.wg0 = wgs;
+    a.wg0[i] = wgs;
+    wgs += s.nwg;
   }
-  if (sizeof(int) * (size_t)words > kSkLdsMax) return hipErrorInvalidValue;
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.T = T;
-  a.lds_words = words;
-  hipLaunchKernelGGL(skinny_kernel<TB>, dim3((unsigned)wgs), dim3(kSkThreads),
-                     sizeof(int) * (size_t)words, stream, a);
+  hipLaunchKernelGGL(skinny_kernel<TB>, dim3((unsigned)wgs), dim3(kSkThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -377,13 +400,9 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
 
 using namespace bl;
 
-bool bl_skinny_supports(int T, int K) { return T >= 1 && T <= 64 && K % 256 == 0; }
+bool bl_skinny_supports(int T, int K) { return T >= 1 && T <= 32 && K % 256 == 0; }
 
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
-  switch ((T + 15) / 16) {
-    case 1: return launch_skinny_t<1>(p, count, T, stream);
-    case 2: return launch_skinny_t<2>(p, count, T, stream);
-    case 3: return launch_skinny_t<3>(p, count, T, stream);
-    default: return launch_skinny_t<4>(p, count, T, stream);
-  }
+  if (T <= 16) return launch_skinny_t<1>(p, count, T, stream);
+  return launch_skinny_t<2>(p, count, T, stream);
 }

@@ -47,11 +47,12 @@ bl_status check_proj(const int8_t* Xq, const float* xs, int64_t T, int64_t K,
 }
 
 bl_kernel choose(int64_t T, int64_t N, int64_t K) {
-  (void)N;
-  // one token: dot4 GEMV; up to 32 tokens: the streaming MFMA kernel; beyond, the
-  // LDS-tiled MFMA GEMM
+  // one token: dot4 GEMV; up to 32 tokens: the streaming MFMA kernel, and up to 128 in
+  // passes of 32 while the GEMM's 128 x 128 tiles would not give every CU two
+  // workgroups; beyond: the LDS-tiled MFMA GEMM
   if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
-  if (bl_skinny_supports((int)T, (int)K)) return BL_KERNEL_SKINNY;
+  const int64_t tiles = ((T + 127) / 128) * ((N + 127) / 128);
+  if (bl_skinny_supports((int)T, (int)K) && (T <= 32 || tiles < 512)) return BL_KERNEL_SKINNY;
   if (bl_prefill_supports((int)T, (int)K)) return BL_KERNEL_PREFILL;
   return BL_KERNEL_GENERIC;
 }

@@ -1,4 +1,4 @@
-// bl_skinny.hip -- ternary x int8 product for 1 < T <= 32 tokens on int8 MFMA
+// bl_skinny.hip -- ternary x int8 product for a few tokens (up to 32 per pass) on int8 MFMA
 // (v_mfma_i32_16x16x64_i8), int32 accumulation, fused rescale.
 //
 // [HF-1.58] "Fine-tuning LLMs to 1.58 bits", "Inference optimization and custom
@@ -49,7 +49,7 @@ constexpr int kSkDepth = 2;                    // steps in flight (weights and a
 constexpr int kSkKS = 512;                     // codes per step
 constexpr int kSkNM = kSkKS / 64;              // MFMAs per step per token block
 constexpr int kSkStepBytes = kSkKS / 4;        // packed bytes per row per step
-constexpr size_t kSkLdsMax = 80 * 1024;        // two workgroups per CU
+constexpr size_t kSkLdsMax = 80 * 1024;  // two workgroups per CU
 
 struct SkProj {
   const int8_t* Xq;
@@ -400,9 +400,25 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
 
 using namespace bl;
 
-bool bl_skinny_supports(int T, int K) { return T >= 1 && T <= 32 && K % 256 == 0; }
+bool bl_skinny_supports(int T, int K) { return T >= 1 && T <= 128 && K % 256 == 0; }
 
+// Up to 32 tokens in one launch; more run as passes over slices of 32 tokens (each pass
+// streams the weights again: the choice of the caller when the GEMM's tiles would
+// leave most of the device idle).
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
-  if (T <= 16) return launch_skinny_t<1>(p, count, T, stream);
-  return launch_skinny_t<2>(p, count, T, stream);
+  for (int t0 = 0; t0 < T; t0 += 32) {
+    const int tn = T - t0 < 32 ? T - t0 : 32;
+    bl_proj_internal q[BL_GROUP_CAP];
+    for (int i = 0; i < count; ++i) {
+      q[i] = p[i];
+      q[i].Xq += (int64_t)t0 * p[i].K;
+      q[i].x_scale += t0;
+      q[i].Y += (int64_t)t0 * p[i].N;
+      if (q[i].acc) q[i].acc += (int64_t)t0 * p[i].N;
+    }
+    const hipError_t e = tn <= 16 ? launch_skinny_t<1>(q, count, tn, stream)
+                                  : launch_skinny_t<2>(q, count, tn, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }

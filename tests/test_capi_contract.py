@@ -180,7 +180,7 @@ def test_forward_validation(lib):
     assert f(A, B, 2, 4096, C, D, 4096, E, None, 1, None) == BL_ERR_ARG  # gemv: T == 1
     assert f(A, B, 1, 4128, C, D, 4096, E, None, 1, None) == BL_ERR_ARG  # gemv: K % 64
     assert f(A, B, 1, 4160, C, D, 4096, E, None, 2, None) == BL_ERR_ARG  # skinny: K % 256
-    assert f(A, B, 33, 4096, C, D, 4096, E, None, 2, None) == BL_ERR_ARG  # skinny: T <= 32
+    assert f(A, B, 129, 4096, C, D, 4096, E, None, 2, None) == BL_ERR_ARG  # skinny: T <= 128
     assert f(A, B, 8, 4160, C, D, 4096, E, None, 3, None) == BL_ERR_ARG  # prefill: K % 128
     assert f(A, B, 1, 4096, C, D, 4096, E, None, 7, None) == BL_ERR_ARG  # no such kernel
 
@@ -194,8 +194,11 @@ def test_dispatch_choice(lib):
     assert f(2, 4096, 4096) == 2
     assert f(16, 4096, 4096) == 2
     assert f(32, 8192, 28672) == 2
-    assert f(33, 8192, 28672) == 3
-    assert f(64, 8192, 28672) == 3
+    assert f(33, 8192, 28672) == 2    # passes of 32: the GEMM would have 64 tiles
+    assert f(64, 8192, 28672) == 2
+    assert f(128, 28672, 8192) == 2   # 224 GEMM tiles: four passes of 32 tokens
+    assert f(129, 28672, 8192) == 3
+    assert f(128, 65536, 4096) == 3   # 512 GEMM tiles
     assert f(2048, 14336, 4096) == 3
     assert f(8, 256, 1028) == 4
 

@@ -172,6 +172,7 @@ PRODUCT_CASES = [
     ("skinny", 1, 300, 4096), ("skinny", 3, 129, 4096), ("skinny", 16, 1000, 14336),
     ("skinny", 17, 257, 8192), ("skinny", 32, 130, 1024), ("skinny", 31, 200, 28672),
     ("skinny", 9, 77, 4352), ("prefill", 33, 130, 1024), ("prefill", 64, 200, 28672),
+    ("skinny", 33, 130, 1024), ("skinny", 100, 200, 4096), ("skinny", 128, 64, 8192),
     ("skinny", 8, 64, 256),
     ("prefill", 1, 130, 1024), ("prefill", 100, 300, 4096), ("prefill", 129, 129, 1280),
     ("prefill", 263, 520, 14336), ("prefill", 256, 256, 128),

@@ -210,9 +210,22 @@ def run_prefill(torch, bl, workloads):
         ms_a = _time_graph(torch, ga, 3) / 16
         ops = 2.0 * T * N * K
         tops = ops / (ms * 1e-3) / 1e12
+        # context: the library int8 GEMM (torch._int_mm) on the same product with the
+        # weights unpacked to one int8 per code (4x the weight bytes)
+        lib = None
+        try:
+            codes = torch.randint(-1, 2, (K, N), dtype=torch.int8, device=dev)
+            gl = _warm_then_capture(torch, [lambda: torch._int_mm(Xq, codes)] * 10)
+            gl.replay()
+            ms_l = _time_graph(torch, gl, 3) / 10
+            lib = round(ops / (ms_l * 1e-3) / 1e12, 1)
+            del codes
+        except (RuntimeError, AttributeError):
+            lib = None
         out.append({"T": T, "N": N, "K": K, "kernel": bl.bitlinear_forward_choice(T, N, K),
                     "ms": round(ms, 5), "tops": round(tops, 1),
                     "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                    "torch_int_mm_tops": lib,
                     "act_quant_ms": round(ms_a, 5),
                     "act_quant_gbs": round(act_bytes(T, K) / (ms_a * 1e-3) / 1e9, 1)})
         del Xs, Xq, Y, packed

@@ -16,7 +16,7 @@
 //      deferred); values further below go into the same accumulator one by one. The
 //      workgroup's digits go to the workspace. This is Kulisch's long-accumulator
 //      idea with a floating window in front of it.
-//   2. wq_finalize: one wave adds the workgroups' digits, propagates carries, and rounds
+//   2. wq_finalize: one workgroup adds the workgroups' digits, propagates carries, and rounds
 //      the exact integer once to fp64 (round to nearest, ties to even): S. Then
 //      gamma = S / (N*K) in fp64 and beta = fp32(gamma).
 //   3. wq_pack: codes q = clamp(rint(w * fp32(1/beta)), -1, 1) (one fp32 product, rint
@@ -102,16 +102,32 @@ __global__ __launch_bounds__(kSumThreads) void wq_abssum(const float4* __restric
   if (tid < kDigits) ws[(int64_t)blockIdx.x * kDigits + tid] = dig[tid];
 }
 
-__global__ __launch_bounds__(64) void wq_finalize(const unsigned long long* __restrict__ ws,
-                                                  int nblocks, int64_t count,
-                                                  float* __restrict__ w_scale,
-                                                  double* __restrict__ w_gamma) {
+__global__ __launch_bounds__(kSumThreads) void wq_finalize(const unsigned long long* __restrict__ ws,
+                                                           int nblocks, int64_t count,
+                                                           float* __restrict__ w_scale,
+                                                           double* __restrict__ w_gamma) {
+  __shared__ unsigned long long part[kDigits][kSumWaves];
   __shared__ unsigned long long col[kDigits];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  // digit columns summed over the workgroups' records: every thread a share of the
+  // records (independent loads), then the waves, then the four wave partials
+  unsigned long long s[kDigits];
+#pragma unroll
+  for (int d = 0; d < kDigits; ++d) s[d] = 0ull;
+  for (int b = tid; b < nblocks; b += kSumThreads)
+#pragma unroll
+    for (int d = 0; d < kDigits; ++d) s[d] += ws[(int64_t)b * kDigits + d];
+#pragma unroll
+  for (int d = 0; d < kDigits; ++d) {
+    const unsigned long long v = wave_sum_u64(s[d]);
+    if (lane == 0) part[d][wave] = v;
+  }
+  __syncthreads();
   if (tid < kDigits) {
-    unsigned long long s = 0ull;
-    for (int b = 0; b < nblocks; ++b) s += ws[(int64_t)b * kDigits + tid];
-    col[tid] = s;
+    unsigned long long c = 0ull;
+#pragma unroll
+    for (int w = 0; w < kSumWaves; ++w) c += part[tid][w];
+    col[tid] = c;
   }
   __syncthreads();
   if (tid != 0) return;
@@ -205,8 +221,8 @@ hipError_t bl_launch_quantize_weights(const float* W, int64_t N, int64_t K, uint
   auto* dig = static_cast<unsigned long long*>(ws);
   hipLaunchKernelGGL(wq_abssum, dim3((unsigned)blocks), dim3(kSumThreads), 0, stream,
                      reinterpret_cast<const float4*>(W), n4, dig);
-  hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(64), 0, stream, dig, (int)blocks, n, w_scale,
-                     w_gamma);
+  hipLaunchKernelGGL(wq_finalize, dim3(1), dim3(kSumThreads), 0, stream, dig, (int)blocks, n,
+                     w_scale, w_gamma);
   int64_t pblocks = (n4 + 1023) / 1024;
   if (pblocks > 4096) pblocks = 4096;
   if (pblocks < 1) pblocks = 1;

@@ -163,21 +163,31 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
 #pragma unroll
   for (int i = 0; i < I; ++i) boff[i] = 16u * (uint32_t)ci[i];
   const uint32_t doff = 16u * (uint32_t)(lane & 3);
-  auto load_w = [&](int g, uint4 (&w)[I]) {
-    const bool real = g <= glast;
-    const int row0 = g * RW;
-    const char* base = reinterpret_cast<const char*>(real ? P.W + (int64_t)row0 * C : dummy);
-    const uint32_t roff = RW == 1 ? 0u : 16u * (uint32_t)((min(row0 + sub, P.N - 1) - row0) * C);
+  // The prefetch walks the row groups with a scalar pointer advanced by a fixed step;
+  // only the last group of a ragged projection (RW > 1) needs the row clamp.
+  const int64_t gstep = (int64_t)stride * RW * C * 16;
+  const char* wnext = reinterpret_cast<const char*>(P.W) + (int64_t)g0 * RW * C * 16;
+  int gnext = g0;
+  auto load_w = [&](uint4 (&w)[I]) {
+    const bool real = gnext <= glast;
+    const char* base = real ? wnext : reinterpret_cast<const char*>(dummy);
+    uint32_t roff = 0u;
+    if constexpr (RW > 1) {
+      const int row0 = gnext * RW;
+      roff = 16u * (uint32_t)((min(row0 + sub, P.N - 1) - row0) * C);
+    }
 #pragma unroll
     for (int i = 0; i < I; ++i)
       w[i] = load_stream(reinterpret_cast<const uint4*>(base + (real ? roff + boff[i] : doff)));
+    wnext += gstep;
+    gnext += stride;
   };
   // The weight ring goes out before the activations: vector loads complete in issue
   // order, so this way the first row waits for one memory latency, not two in a row.
   // The two scales come through the scalar cache, off the vector counter.
   uint4 w[kGemvDepth][I];
 #pragma unroll
-  for (int d = 0; d < kGemvDepth; ++d) load_w(g0 + d * stride, w[d]);
+  for (int d = 0; d < kGemvDepth; ++d) load_w(w[d]);
   uint4 x[I][4];
   int xsum = 0;
 #pragma unroll
@@ -205,7 +215,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
     Acc4 s{-xsum, 0, 0};
 #pragma unroll
     for (int i = 0; i < I; ++i) dot_chunk(w[d][i], x[i], s);
-    if (prefetch) load_w(g + kGemvDepth * stride, w[d]);
+    if (prefetch) load_w(w[d]);
     int tot = group_sum_to_last<L>(acc_total(s));
     if constexpr (S > 1) {
       // the S segment sums of this row meet in one LDS word; the wave that completes

@@ -70,8 +70,8 @@ typedef enum bl_status {
 typedef enum bl_kernel {
   BL_KERNEL_AUTO = 0,
   BL_KERNEL_GEMV = 1,     /* decode GEMV, int8 dot4; needs T == 1 and K % 64 == 0 */
-  BL_KERNEL_SKINNY = 2,   /* skinny int8 MFMA GEMM; needs T <= 128 and K % 256 == 0
-                             (passes of 32 tokens) */
+  BL_KERNEL_SKINNY = 2,   /* skinny int8 MFMA GEMM; needs T <= 128, K % 256 == 0 and
+                             N < 2^24 (passes of 32 tokens) */
   BL_KERNEL_PREFILL = 3,  /* LDS-tiled int8 MFMA GEMM; needs K % 128 == 0 */
   BL_KERNEL_GENERIC = 4   /* any K % 4 == 0, any T: one thread per output */
 } bl_kernel;

@@ -52,15 +52,15 @@ bl_kernel choose(int64_t T, int64_t N, int64_t K) {
   // workgroups; beyond: the LDS-tiled MFMA GEMM
   if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
   const int64_t tiles = ((T + 127) / 128) * ((N + 127) / 128);
-  if (bl_skinny_supports((int)T, (int)K) && (T <= 32 || tiles < 512)) return BL_KERNEL_SKINNY;
+  if (bl_skinny_supports((int)T, N, (int)K) && (T <= 32 || tiles < 512)) return BL_KERNEL_SKINNY;
   if (bl_prefill_supports((int)T, (int)K)) return BL_KERNEL_PREFILL;
   return BL_KERNEL_GENERIC;
 }
 
-bool supports(bl_kernel k, int64_t T, int64_t K) {
+bool supports(bl_kernel k, int64_t T, int64_t N, int64_t K) {
   switch (k) {
     case BL_KERNEL_GEMV: return bl_gemv_supports((int)T, (int)K);
-    case BL_KERNEL_SKINNY: return bl_skinny_supports((int)T, (int)K);
+    case BL_KERNEL_SKINNY: return bl_skinny_supports((int)T, N, (int)K);
     case BL_KERNEL_PREFILL: return bl_prefill_supports((int)T, (int)K);
     case BL_KERNEL_GENERIC: return true;
     default: return false;
@@ -144,7 +144,7 @@ bl_status bitlinear_forward_ex(const int8_t* Xq, const float* x_scale, int64_t T
   bl_status s = check_proj(Xq, x_scale, T, K, W_packed, w_scale, N, Y, acc);
   if (s != BL_OK) return s;
   if (kernel == BL_KERNEL_AUTO) kernel = choose(T, N, K);
-  if (!supports(kernel, T, K)) return BL_ERR_ARG;
+  if (!supports(kernel, T, N, K)) return BL_ERR_ARG;
   bl_proj_internal p = to_internal(Xq, x_scale, K, W_packed, w_scale, N, Y, acc);
   (void)hipGetLastError();
   return hip_status(run(kernel, &p, 1, (int)T, (hipStream_t)stream));

@@ -30,7 +30,7 @@ hipError_t bl_launch_quantize_acts(const bl_act_desc* d, int count, int64_t T, f
 // Product kernels: each takes 1..BL_GROUP_CAP projections sharing T.
 bool bl_gemv_supports(int T, int K);
 hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream);
-bool bl_skinny_supports(int T, int K);
+bool bl_skinny_supports(int T, int64_t N, int K);
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream);
 bool bl_prefill_supports(int T, int K);
 hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream);

@@ -7,32 +7,32 @@
 // operation": rescale by the weight and activation scales.
 //
 // With few tokens the product is bound by the packed-weight stream (2 ops per weight per
-// token against 1/4 byte per weight): every weight byte is read from HBM once, straight
-// into registers, by waves that keep a ring of loads in flight.
-//   - A workgroup has 8 waves: S teams (S = 1, 2 or 4) of G = 8/S waves. Team s owns
-//     the s-th of S contiguous K segments; its G waves own G row blocks of 16 rows. A
-//     step is 512 codes: per row block a lane loads 32 bytes (row lane % 16, bytes
-//     32*(lane/16) of the step's 128) with two 128-bit loads, so every instruction pair
-//     reads whole 128-byte lines, and feeds eight MFMAs.
-//   - The activations of a step (16*TB tokens x 512 codes per team) are loaded once per
-//     workgroup, coalesced, by all 512 threads, each step's ahead of its weights (so
-//     that waiting for them never waits for those weights),
-//     4x4 byte-transposed to the unpack order and written to one of two LDS stages, laid
-//     out so that each MFMA's B operand is one conflict-free 1 KB read. One barrier per
-//     step hands a stage from writers to readers; the weight loads in flight are not
-//     waited for there.
-//   - MFMA j of a step takes codes 64j + 16*ks for lane k-slot ks: each token's four
-//     lanes read 64 contiguous staged bytes. The A operand of MFMA j at lane (row, ks) is
-//     the packed dword at byte 16j + 4ks of the row's 128 bytes, which lane (row, j / 2)
-//     loaded as its register 4*(j % 2) + ks: two 4x4 transposes across the four lane
-//     rows (v_permlane32_swap, v_permlane16_swap) bring them over, and unpack_u2 gives
-//     u = q + 1 in p-major order.
-//   - sum x*u - sum x = sum x*q: the activation sum comes from one more MFMA per B
-//     operand with an all-ones A operand.
-//   - The S teams' partial tiles meet in LDS at the end of each row-block iteration;
-//     team 0 rescales and stores Y = fp32(acc) * fp32(beta / s_t).
+// token against 1/4 byte per weight). The activations are the only reused operand and
+// they are small (T x K bytes), so each wave keeps its share of them in registers and
+// streams weight rows past them, like the decode GEMV:
+//   - K is cut into segments of 256*MPW codes (MPW = 1, 2, 4 or 7). A workgroup has 8
+//     waves: teams of S waves, wave s of a team owning segment s (with more segments
+//     than S, the team makes several passes, reloading its activations per pass).
+//   - Per wave and segment, the MFMA B operands (16 tokens x 64 codes each: lane (token
+//     t, k-slot g) holds 16 activation bytes) live in registers for the whole sweep.
+//     They are 4x4 byte-transposed to the order in which a packed dword unpacks, and
+//     the code -> k-slot assignment is chosen so that a lane's own 128-bit weight load
+//     (row lane % 16, bytes 64m + 16g of the segment) is directly the A operand of four
+//     MFMAs: no cross-lane exchange of weights.
+//   - A team sweeps its row blocks (16 rows each); per row block every wave loads 16
+//     rows x 64*MPW bytes with MPW 128-bit buffer loads per lane, kept in a ring D row
+//     blocks deep (non-temporal; rows past N and codes past K fall outside the buffer
+//     range, so they read as zeros without a memory access or a branch), unpacks
+//     u = q + 1 and issues 4*MPW MFMAs per token block, starting from -sum(x) of its
+//     segment (sum x*u - sum x = sum x*q; the sum is one MFMA per B operand with an
+//     all-ones A, once per pass).
+//   - The S partial 16x16 tiles of a row block meet in LDS by ds_add (integer, so the
+//     order of arrival does not matter), followed by one arrival count per wave; the
+//     wave whose arrival completes the count reads the tile back and stores
+//     Y = fp32(acc) * fp32(beta / s_t). No barrier after the start: every row block has
+//     its own tile for the whole launch (more workgroups when they would not fit).
 //   - Workgroups are partitioned among the projections of a grouped call in proportion
-//     to their bytes; the grid is one round of resident workgroups.
+//     to their bytes, normally one round of resident workgroups.
 // MFMA output: lane l, register r holds row 4*(l/16) + r of the block, token l % 16.
 #include "bl_device.h"
 #include "bl_internal.h"
@@ -45,11 +45,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;  // 512
-constexpr int kSkDepth = 2;                    // steps in flight (weights and activations)
-constexpr int kSkKS = 512;                     // codes per step
-constexpr int kSkNM = kSkKS / 64;              // MFMAs per step per token block
-constexpr int kSkStepBytes = kSkKS / 4;        // packed bytes per row per step
-constexpr size_t kSkLdsMax = 80 * 1024;  // two workgroups per CU
+constexpr int kSkTileKB = 96;  // LDS for the partial tiles of a workgroup's row blocks, KiB
+constexpr size_t kSkLdsMax = kSkTileKB * 1024 + 96 * 4 + 32 * 4;
 
 struct SkProj {
   const int8_t* Xq;
@@ -59,9 +56,13 @@ struct SkProj {
   float* Y;
   int32_t* acc;
   int N, K;
-  int steps;    // ceil(K / 512)
+  int nrb;       // row blocks of 16
+  int mpw;       // a segment is 256 * mpw codes: mpw 128-bit loads per lane and row block
+  int nseg;      // segments covering K
+  int S, teams;  // waves per team, teams per workgroup
+  int npass;     // passes of a team over the segments
+  int R;         // row blocks per team
   int wg0, nwg;
-  int S, CW;    // teams (K segments) and steps per segment
 };
 
 struct SkArgs {
@@ -83,223 +84,217 @@ __device__ __forceinline__ SkProj load_sk(SkArgsPtr a, int i) {
   P.acc = a->p[i].acc;
   P.N = a->p[i].N;
   P.K = a->p[i].K;
-  P.steps = a->p[i].steps;
+  P.nrb = a->p[i].nrb;
+  P.mpw = a->p[i].mpw;
+  P.nseg = a->p[i].nseg;
+  P.S = a->p[i].S;
+  P.teams = a->p[i].teams;
+  P.npass = a->p[i].npass;
+  P.R = a->p[i].R;
   P.wg0 = a->p[i].wg0;
   P.nwg = a->p[i].nwg;
-  P.S = a->p[i].S;
-  P.CW = a->p[i].CW;
   return P;
 }
 
-// 4x4 transpose of dwords across the four 16-lane rows: on return, register q of lane
-// (row s) holds what register s of lane (row q) held.
-__device__ __forceinline__ void transpose_rows(uint32_t (&r)[4]) {
-  auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
-  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  r[0] = c[0];
-  r[1] = c[1];
-  r[2] = d[0];
-  r[3] = d[1];
+// Position of (token, row) in a 16 x 16 tile of ints: rows of one token are contiguous,
+// XOR-swizzled so that the 64 lanes of one ds_add (4 rows x 16 tokens) hit distinct
+// banks, both as 64 banks and as two halves of 32.
+__device__ __forceinline__ int sk_pos(int tok, int row) {
+  const int h = ((tok >> 2) & 3) | (((tok >> 1) & 1) << 3);
+  return tok * 16 + (row ^ h);
 }
 
-// LDS bytes of one stage and of a whole workgroup, per team count S and token blocks TB.
-__host__ __device__ constexpr int sk_stage_bytes(int S, int TB) { return S * kSkNM * TB * 1024; }
-__host__ __device__ constexpr int sk_lds_bytes(int S, int TB) {
-  return 2 * sk_stage_bytes(S, TB) + kSkWaves * TB * 1024;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: reads 0, drops writes
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
-template <int TB, int S>
-__device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wave, uint8_t* lds) {
-  constexpr int G = kSkWaves / S;
-  constexpr int D = kSkDepth;
-  constexpr int PIECES = S * 16 * TB * (kSkKS / 16);  // 16-byte activation pieces per step
-  constexpr int PPT = (PIECES + kSkThreads - 1) / kSkThreads;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), li = lane & 15, lg = lane >> 4;
-  const int seg = wave / G, mem = wave % G;
-  const int nrb = (P.N + 15) / 16;
-  // every wave of the workgroup runs the same number of steps (one barrier per step)
-  const int niter = (nrb - wgl * G + P.nwg * G - 1) / (P.nwg * G);
-  const int CW = P.CW;
-  const int total = niter * CW;
+template <int TB, int MPW, int D>
+__device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wave, int* tiles,
+                                         int* counts, const float* facs) {
+  const int lane = threadIdx.x & (kWave - 1), li = lane & 15, lg = lane >> 4;
+  const int S = P.S, teams = P.teams;
+  const int team = wave / S;
+  const int seg = wave - team * S;
+  const int R = P.R, npass = P.npass;
+  const int nsteps = npass * R;
+  const int target = S * npass;  // arrivals that complete a row block
+  const int TT = P.nwg * teams;  // teams over the projection
+  const int tg = wgl * teams + team;
   const int Kb = P.K >> 2;
-  uint8_t* stage0 = lds;
-  uint8_t* stage1 = lds + sk_stage_bytes(S, TB);
-  int* comb = reinterpret_cast<int*>(lds + 2 * sk_stage_bytes(S, TB));
+  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  const Rsrc xr = make_rsrc(P.Xq, (uint32_t)T * (uint32_t)P.K);
+  const Rsrc yr = make_rsrc(P.Y, (uint32_t)T * (uint32_t)P.N * 4u);
+  const Rsrc ar = make_rsrc(P.acc, P.acc ? (uint32_t)T * (uint32_t)P.N * 4u : 0u);
 
-  // activation pieces this thread stages: piece q = tid + p * 512 -> team, token, offset
-  int pt_tok[PPT], pt_seg[PPT], pt_off[PPT], pt_lds[PPT];
-  bool pt_on[PPT];
+  // B operands of this wave's segment in pass p (padding tokens and codes past K read
+  // as zeros through the buffer range), then minus their per-token sums
+  uint4 braw[MPW][4][TB];
+  v4i B[MPW][4][TB];
+  v4i ncs[TB];
+  auto issue_B = [&](int p) {
+    const int sg = p * S + seg;
 #pragma unroll
-  for (int p = 0; p < PPT; ++p) {
-    const int q = tid + p * kSkThreads;
-    pt_on[p] = q < PIECES;
-    const int qq = pt_on[p] ? q : 0;
-    const int o16 = qq % (kSkKS / 16);
-    const int t = (qq / (kSkKS / 16)) % (16 * TB);
-    const int s = qq / ((kSkKS / 16) * 16 * TB);
-    pt_tok[p] = min(t, T - 1);  // tokens past T: any valid row (their columns are dropped)
-    pt_seg[p] = s;
-    pt_off[p] = 16 * o16;
-    const int j = o16 >> 2, ks = o16 & 3;
-    pt_lds[p] = ((((s * kSkNM + j) * TB + (t >> 4)) * kWave) + ks * 16 + (t & 15)) * 16;
-  }
-  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(P.Xq);
-
-  uint4 w[D][2];
-  uint4 xr[D][PPT];
-  // weights of step n (iteration n / CW, segment step n % CW) into ring slot d: this
-  // wave's row block, its team's segment; lanes past the row end read a dummy block
-  auto load_w = [&](int n, int d) {
-    const int it = n / CW, m = n - it * CW;
-    const int rb = (wgl + it * P.nwg) * G + mem;
-    const int st = seg * CW + m;
-    const bool real = n < total && st * kSkKS + 128 * lg < P.K;
-    const int row = min(rb * 16 + li, P.N - 1);
-    const uint8_t* wp =
-        real ? P.W + (int64_t)row * Kb + st * kSkStepBytes + 32 * lg : dummy + 32 * (lane & 3);
-    w[d][0] = *reinterpret_cast<const uint4*>(wp);
-    w[d][1] = *reinterpret_cast<const uint4*>(wp + 16);
-  };
-  // activations of step n into slot d: pieces of every team's step (past the row end,
-  // any valid bytes: they are replaced by zeros when staged)
-  auto load_x = [&](int n, int d) {
-    const int m = n - (n / CW) * CW;
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      if (!pt_on[p]) continue;  // wave-uniform: pieces come in whole waves
-      const int code = min((pt_seg[p] * CW + m) * kSkKS + pt_off[p], P.K - 16);
-      xr[d][p] = *reinterpret_cast<const uint4*>(P.Xq + (int64_t)pt_tok[p] * P.K + code);
-    }
-  };
-  // staged activations of step n (from slot d), transposed; zero past the row end
-  auto stage = [&](int n, int d, uint8_t* dst) {
-    const int m = n - (n / CW) * CW;
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      if (!pt_on[p]) continue;
-      uint4 v = xr[d][p];
-      if ((pt_seg[p] * CW + m) * kSkKS + pt_off[p] >= P.K) v = make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
-      transpose16(in, o);
-      *reinterpret_cast<uint4*>(dst + pt_lds[p]) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  };
-
-  v4i acc[TB], cs[TB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    acc[tb] = v4i{0, 0, 0, 0};
-    cs[tb] = v4i{0, 0, 0, 0};
-  }
-  typedef const float __attribute__((address_space(4)))* ConstF;
-  const float beta = *(ConstF)P.ws;
-  float fac[TB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) fac[tb] = beta / P.xs[min(16 * tb + li, T - 1)];
-
-  // end of a row-block iteration: teams meet in LDS, team 0 stores
-  auto finish = [&](int it) {
-    if constexpr (S > 1) {
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          comb[(((seg * G + mem) * TB + tb) * 4 + r) * kWave + lane] = acc[tb][r] - cs[tb][r];
-      __syncthreads();
-    }
-    if (seg == 0) {
-      const int row0 = ((wgl + it * P.nwg) * G + mem) * 16;
+    for (int m = 0; m < MPW; ++m)
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        v4i v = acc[tb] - cs[tb];
-#pragma unroll
-        for (int s2 = 1; s2 < S; ++s2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] += comb[(((s2 * G + mem) * TB + tb) * 4 + r) * kWave + lane];
         const int tok = 16 * tb + li;
-        if (tok < T) {
+        const int code = (sg * MPW + m) * 256 + 64 * lg;
+        const bool ok = sg < P.nseg && tok < T && code < P.K;
+        const uint32_t off = ok ? (uint32_t)tok * (uint32_t)P.K + (uint32_t)code : kOob;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4i v = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16 * i, 0, 0);
+          braw[m][i][tb] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+        }
+      }
+  };
+  auto finish_B = [&]() {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const uint4 v = braw[m][i][tb];
+          const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+          uint32_t o[4];
+          transpose16(in, o);
+          B[m][i][tb] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      v4i c = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < MPW; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, B[m][i][tb], c, 0, 0, 0);
+      ncs[tb] = v4i{0, 0, 0, 0} - c;
+    }
+  };
+
+  // weight ring: row block rb as a buffer of its (up to) 16 rows, empty past the matrix;
+  // the prefetch position (pass, row-block ordinal) advances per load
+  uint4 w[D][MPW];
+  int fn = 0, fr = 0, fp = 0;
+  auto load_w = [&](int d) {
+    const int rb = tg + fr * TT;
+    const int sg = fp * S + seg;
+    const bool valid = fn < nsteps && rb < P.nrb && sg < P.nseg;
+    const int rows = valid ? min(16, P.N - rb * 16) : 0;
+    const Rsrc wr = make_rsrc(P.W + (valid ? (int64_t)rb * 16 * Kb : 0), (uint32_t)(rows * Kb));
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const int byte = (sg * MPW + m) * 64 + 16 * lg;
+      const uint32_t off = byte < Kb ? (uint32_t)(li * Kb + byte) : kOob;
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // non-temporal
+      w[d][m] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+    }
+    ++fn;
+    if (++fr == R) {
+      fr = 0;
+      ++fp;
+    }
+  };
+
+  // activations first (L2-resident), then the weight ring; the activation registers are
+  // rearranged while the weights are still in flight
+  issue_B(0);
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(d);
+  finish_B();
+
+  const bool vec_store = (P.N & 3) == 0;
+  int cr = 0, cp = 0;
+  auto step = [&](int d, bool prefetch) {
+    v4i acc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[tb] = ncs[tb];
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const uint32_t wd[4] = {w[d][m].x, w[d][m].y, w[d][m].z, w[d][m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t u[4];
+        unpack_u2(wd[i], u);
+        const v4i ua = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+          acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, B[m][i][tb], acc[tb], 0, 0, 0);
+      }
+    }
+    if (prefetch) load_w(d);
+    // partial tile into LDS, then one arrival; the wave that completes the count owns
+    // the sum (every earlier arrival's adds were performed before its count)
+    const int slot = team * R + cr;
+    int* tile = tiles + slot * TB * 256;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __hip_atomic_fetch_add(tile + tb * 256 + sk_pos(li, 4 * lg + r), acc[tb][r],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(counts + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == target - 1) {
+      const int rb = tg + cr * TT;
+      const int row = rb * 16 + 4 * lg;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int t = 16 * tb + li;
+        int v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[r] = __hip_atomic_load(tile + tb * 256 + sk_pos(li, 4 * lg + r), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        const float f = facs[t];
+        const bool tin = t < T;
+        if (vec_store) {
+          const uint32_t off = tin && row < P.N ? ((uint32_t)t * (uint32_t)P.N + (uint32_t)row) * 4u : kOob;
+          const v4i y = v4i{__float_as_int((float)v[0] * f), __float_as_int((float)v[1] * f),
+                            __float_as_int((float)v[2] * f), __float_as_int((float)v[3] * f)};
+          __builtin_amdgcn_raw_buffer_store_b128(y, yr, off, 0, 0);
+          if (P.acc) __builtin_amdgcn_raw_buffer_store_b128(v4i{v[0], v[1], v[2], v[3]}, ar, off, 0, 0);
+        } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = row0 + 4 * lg + r;
-            if (row < P.N) {
-              P.Y[(int64_t)tok * P.N + row] = (float)v[r] * fac[tb];
-              if (P.acc) P.acc[(int64_t)tok * P.N + row] = v[r];
-            }
+            const uint32_t off =
+                tin && row + r < P.N ? ((uint32_t)t * (uint32_t)P.N + (uint32_t)(row + r)) * 4u : kOob;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int((float)v[r] * f), yr, off, 0, 0);
+            if (P.acc) __builtin_amdgcn_raw_buffer_store_b32(v[r], ar, off, 0, 0);
           }
         }
       }
     }
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      acc[tb] = v4i{0, 0, 0, 0};
-      cs[tb] = v4i{0, 0, 0, 0};
-    }
-  };
-
-  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  // prologue: steps 0 and 1 in flight, each step's activations ahead of its weights
-  // (waiting for the activations of a step never waits for its weights); step 0 staged
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_x(d, d);
-    load_w(d, d);
-  }
-  stage(0, 0, stage0);
-  __syncthreads();
-
-  // step n consumes ring slot and stage n % 2, issues step n + 2 into that slot and
-  // stages step n + 1 from the other one
-  auto step = [&](int n, int d, bool prefetch) {
-    uint8_t* cur = d ? stage1 : stage0;
-    uint8_t* nxt = d ? stage0 : stage1;
-    // A operands: MFMA j's dword ks sits in lane row j / 2, register 4 * (j % 2) + ks
-    uint32_t a0[4] = {w[d][0].x, w[d][0].y, w[d][0].z, w[d][0].w};
-    uint32_t a1[4] = {w[d][1].x, w[d][1].y, w[d][1].z, w[d][1].w};
-    transpose_rows(a0);
-    transpose_rows(a1);
-#pragma unroll
-    for (int j = 0; j < kSkNM; ++j) {
-      uint32_t u[4];
-      unpack_u2((j & 1) ? a1[j >> 1] : a0[j >> 1], u);
-      const v4i ua = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const uint4 bx = *reinterpret_cast<const uint4*>(
-            cur + (((seg * kSkNM + j) * TB + tb) * kWave + lane) * 16);
-        const v4i bv = v4i{(int)bx.x, (int)bx.y, (int)bx.z, (int)bx.w};
-        acc[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, bv, acc[tb], 0, 0, 0);
-        cs[tb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, bv, cs[tb], 0, 0, 0);
+    if (++cr == R) {
+      cr = 0;
+      ++cp;
+      if (npass > 1 && cp < npass) {
+        issue_B(cp);
+        finish_B();
       }
     }
-    if (prefetch) {
-      load_x(n + D, d);
-      load_w(n + D, d);
-    }
-    if (n + 1 < total) stage(n + 1, d ^ 1, nxt);
-    const int it = n / CW;
-    if (n - it * CW == CW - 1) finish(it);
-    __syncthreads();
   };
-  // whole rounds of D steps, then the rest: every wave of the workgroup runs the same
-  // steps, so every barrier is reached by all of them
+  // whole rounds of D steps, then the rest (single exit, static ring slots)
   int n = 0;
-  while (total - n >= D) {
+  while (nsteps - n >= D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) step(n + d, d, true);
+    for (int d = 0; d < D; ++d) step(d, true);
     n += D;
   }
 #pragma unroll
   for (int d = 0; d < D - 1; ++d)
-    if (n + d < total) step(n + d, d, false);
+    if (n + d < nsteps) step(d, false);
 }
 
 template <int TB>
 __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
-  extern __shared__ uint4 sk_lds[];
+  extern __shared__ int sk_lds[];
   const SkArgsPtr a = (SkArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
   const int wg = (int)blockIdx.x;
   int pi = 0;
@@ -309,12 +304,24 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   const int T = a->T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wgl = wg - P.wg0;
-  uint8_t* lds = reinterpret_cast<uint8_t*>(sk_lds);
-  switch (P.S) {
-    case 1: sk_sweep<TB, 1>(P, T, wgl, wave, lds); break;
-    case 2: sk_sweep<TB, 2>(P, T, wgl, wave, lds); break;
+  const int nslot = P.teams * P.R;
+  int* tiles = sk_lds;
+  int* counts = sk_lds + nslot * TB * 256;
+  float* facs = reinterpret_cast<float*>(counts + nslot);
+  for (int i = threadIdx.x; i < nslot * (TB * 256 + 1); i += kSkThreads) sk_lds[i] = 0;
+  if (threadIdx.x < 16 * TB) {
+    typedef const float __attribute__((address_space(4)))* ConstF;
+    const float beta = *(ConstF)P.ws;
+    facs[threadIdx.x] = beta / P.xs[min((int)threadIdx.x, T - 1)];
+  }
+  __syncthreads();
+  if (wave >= P.S * P.teams) return;  // leftover waves: no segment (no barrier follows)
+  switch (P.mpw) {
+    case 1: sk_sweep<TB, 1, 4>(P, T, wgl, wave, tiles, counts, facs); break;
+    case 2: sk_sweep<TB, 2, 4>(P, T, wgl, wave, tiles, counts, facs); break;
+    case 4: sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs); break;
     default:
-      if constexpr (TB == 1) sk_sweep<TB, 4>(P, T, wgl, wave, lds);
+      if constexpr (TB == 1) sk_sweep<TB, 7, 2>(P, T, wgl, wave, tiles, counts, facs);
       break;
   }
 }
@@ -336,13 +343,29 @@ int sk_resident(size_t lds) {
   return cus * per;
 }
 
-// Teams per row block: segments of at least 4 steps, more teams while the row blocks
-// alone would leave the device short of waves.
-int sk_teams(int steps, int nrb, int TB) {
-  const int smax = TB == 1 ? 4 : 2;  // keeps the stages and the combine area within 80 KB
-  int S = 1;
-  while (S < smax && steps / (2 * S) >= 4 && nrb * S < 4096) S *= 2;
-  return S;
+// Segment length and team shape for K: the largest fraction of wave-steps spent on real
+// codes (segments past K, idle waves and passes that leave waves without a segment
+// count as waste); ties go to the longer segment.
+void sk_plan(int K, int TB, SkProj& s) {
+  const int c = K / 256;
+  const int cand[4] = {7, 4, 2, 1};
+  double best = -1.0;
+  for (int m : cand) {
+    if (TB == 2 && m > 4) continue;
+    const int nseg = (c + m - 1) / m;
+    const int S = nseg < kSkWaves ? nseg : kSkWaves;
+    const int teams = kSkWaves / S;
+    const int npass = (nseg + S - 1) / S;
+    const double e = (double)teams * c / ((double)kSkWaves * m * npass);
+    if (e > best + 1e-9) {
+      best = e;
+      s.mpw = m;
+      s.nseg = nseg;
+      s.S = S;
+      s.teams = teams;
+      s.npass = npass;
+    }
+  }
 }
 
 // The dynamic-LDS limit is raised once per instance (first launch), never inside a
@@ -354,7 +377,6 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
   if (attr != hipSuccess) return attr;
   SkArgs a{};
   int64_t total = 0;
-  size_t lds = 0;
   for (int i = 0; i < count; ++i) {
     SkProj& s = a.p[i];
     s.Xq = p[i].Xq;
@@ -365,30 +387,38 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
     s.acc = p[i].acc;
     s.N = p[i].N;
     s.K = p[i].K;
-    s.steps = (p[i].K + kSkKS - 1) / kSkKS;
-    s.S = sk_teams(s.steps, (s.N + 15) / 16, TB);
-    s.CW = (s.steps + s.S - 1) / s.S;
-    const size_t need = (size_t)sk_lds_bytes(s.S, TB);
-    lds = need > lds ? need : lds;
+    s.nrb = (p[i].N + 15) / 16;
+    sk_plan(p[i].K, TB, s);
     total += (int64_t)p[i].N * (p[i].K / 4);
   }
-  if (lds > kSkLdsMax) return hipErrorInvalidValue;
-  const int cap = sk_resident<TB>(lds);
+  // the occupancy does not depend on the LDS size up to the cap (registers bound it)
+  const int cap = sk_resident<TB>(kSkLdsMax);
   int wgs = 0;
+  size_t lds = 0;
   for (int i = 0; i < count; ++i) {
     SkProj& s = a.p[i];
-    const int G = kSkWaves / s.S;
-    const int nrb = (s.N + 15) / 16;
     const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
-    int64_t n = (bytes * (int64_t)(cap - count) + total - 1) / total;
+    int64_t n = (bytes * (int64_t)(cap - count + 1) + total - 1) / total;
     n = n < 1 ? 1 : n;
-    const int64_t most = (nrb + G - 1) / G;  // no workgroup without a row block
+    // every row block of a team keeps its tile in LDS until it is complete: more
+    // workgroups (beyond one resident round) when the tiles would not fit
+    const int rcap = kSkTileKB / (s.teams * TB);
+    const int64_t need_wg = (s.nrb + (int64_t)s.teams * rcap - 1) / ((int64_t)s.teams * rcap);
+    n = n < need_wg ? need_wg : n;
+    const int64_t most = (s.nrb + s.teams - 1) / s.teams;  // no workgroup without a row block
     n = n > most ? most : n;
+    // as few workgroups as give the same number of row blocks per team
+    const int64_t jmax = (s.nrb + n * s.teams - 1) / (n * s.teams);
+    n = (s.nrb + jmax * s.teams - 1) / (jmax * s.teams);
     s.nwg = (int)n;
+    s.R = (int)jmax;
     s.wg0 = wgs;
     a.wg0[i] = wgs;
     wgs += s.nwg;
+    const size_t need = (size_t)s.teams * s.R * (TB * 1024 + 4) + 16 * TB * sizeof(float);
+    lds = need > lds ? need : lds;
   }
+  if (lds > kSkLdsMax) return hipErrorInvalidValue;
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.T = T;
@@ -400,7 +430,10 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
 
 using namespace bl;
 
-bool bl_skinny_supports(int T, int K) { return T >= 1 && T <= 128 && K % 256 == 0; }
+// Output offsets of one pass (32 tokens) are 32-bit buffer offsets.
+bool bl_skinny_supports(int T, int64_t N, int K) {
+  return T >= 1 && T <= 128 && K % 256 == 0 && N * 32 * 4 < (int64_t(1) << 31);
+}
 
 // Up to 32 tokens in one launch; more run as passes over slices of 32 tokens (each pass
 // streams the weights again: the choice of the caller when the GEMM's tiles would

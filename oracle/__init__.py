@@ -17,6 +17,14 @@ step, the passage of the pages it follows and the precision of every rounding:
   6. acc = Xq . codes^T in integers
   7. Y = fp32(acc * beta / s_t) computed in fp64
 
+and the 1-bit sign variant (the original BitNet weight binarization):
+
+  S1. alpha = exact sum W / (N*K) in fp64
+  S2. codes = +1 where fp64(w) > alpha, else -1 (Sign(0) = -1)
+  S3. beta = fp32(mean |W|) (step 1's scale)
+  S4. eight codes per byte, code k = 8j+i in bit i of byte j, set for +1
+  S5. acc = Xq . codes^T in integers, Y = fp32(acc * beta / s_t)
+
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (brute force in exact rationals, library routines, closed forms, invariants and the
 worked examples under ``tests/golden/``).
@@ -86,6 +94,13 @@ def _load():
                 "orc_product": [P, P, I64, I64, I64, P],
                 "orc_rescale": [P, P, ctypes.c_float, I64, I64, P],
                 "orc_forward": [P, P, I64, I64, P, ctypes.c_float, I64, P, P],
+                "orc_sum": [P, I64, P],
+                "orc_sign_codes": [P, I64, ctypes.c_double, P],
+                "orc_sign_weights": [P, I64, I64, P, P, P, P],
+                "orc_pack1": [P, I64, I64, P],
+                "orc_unpack1": [P, I64, I64, P],
+                "orc_product_sign": [P, P, I64, I64, I64, P],
+                "orc_forward_sign": [P, P, I64, I64, P, ctypes.c_float, I64, P, P],
             }
             for name, args in sig.items():
                 f = getattr(lib, name)
@@ -244,3 +259,83 @@ def bitlinear(X, W, gain=None, eps=1e-6, flags=0):
     Y, acc = forward(Xq, s, P, beta)
     return {"packed": P, "beta": beta, "gamma": gamma, "Xq": Xq, "x_scale": s,
             "acc": acc, "Y": Y}
+
+
+# ---------------------------------------------------------------- sign variant
+
+def exact_sum(w) -> float:
+    """Exact signed sum rounded once to fp64."""
+    w = _f32(w)
+    out = ctypes.c_double()
+    _check(_load().orc_sum(_ptr(w), w.size, ctypes.addressof(out)))
+    return out.value
+
+
+def sign_codes(W, alpha):
+    W = _f32(W)
+    c = np.empty(W.shape, dtype=np.int8)
+    _check(_load().orc_sign_codes(_ptr(W), W.size, float(alpha), _ptr(c)))
+    return c
+
+
+def sign_weights(W):
+    """W [N, K] fp32 -> (codes int8 [N, K] in {-1, +1}, alpha fp64, gamma fp64, beta fp32)."""
+    W = _f32(W)
+    N, K = W.shape
+    c = np.empty((N, K), dtype=np.int8)
+    a = ctypes.c_double()
+    g = ctypes.c_double()
+    b = ctypes.c_float()
+    _check(_load().orc_sign_weights(_ptr(W), N, K, _ptr(c), ctypes.addressof(a),
+                                    ctypes.addressof(g), ctypes.addressof(b)))
+    return c, a.value, g.value, np.float32(b.value)
+
+
+def pack1(c):
+    c = np.ascontiguousarray(c, dtype=np.int8)
+    N, K = c.shape
+    P = np.empty((N, K // 8), dtype=np.uint8)
+    _check(_load().orc_pack1(_ptr(c), N, K, _ptr(P)))
+    return P
+
+
+def unpack1(P, K):
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    N = P.shape[0]
+    c = np.empty((N, K), dtype=np.int8)
+    _check(_load().orc_unpack1(_ptr(P), N, K, _ptr(c)))
+    return c
+
+
+def product_sign(Xq, P, K):
+    Xq = np.ascontiguousarray(Xq, dtype=np.int8)
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    T = Xq.shape[0]
+    N = P.shape[0]
+    acc = np.empty((T, N), dtype=np.int32)
+    _check(_load().orc_product_sign(_ptr(Xq), _ptr(P), T, N, K, _ptr(acc)))
+    return acc
+
+
+def forward_sign(Xq, s, P, beta):
+    """(Xq [T,K], s [T], packed bits [N,K/8], beta) -> (Y fp32 [T,N], acc int32 [T,N])."""
+    Xq = np.ascontiguousarray(Xq, dtype=np.int8)
+    s = _f32(s)
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    T, K = Xq.shape
+    N = P.shape[0]
+    Y = np.empty((T, N), dtype=np.float32)
+    acc = np.empty((T, N), dtype=np.int32)
+    _check(_load().orc_forward_sign(_ptr(Xq), _ptr(s), T, K, _ptr(P), float(np.float32(beta)),
+                                    N, _ptr(Y), _ptr(acc)))
+    return Y, acc
+
+
+def bitlinear_sign(X, W, gain=None, eps=1e-6, flags=0):
+    """The 1-bit sign forward from fp32 X [T,K] and W [N,K]; returns a dict of stages."""
+    c, alpha, gamma, beta = sign_weights(W)
+    P = pack1(c)
+    Xq, s = quantize_acts(X, gain, eps, flags)
+    Y, acc = forward_sign(Xq, s, P, beta)
+    return {"packed": P, "codes": c, "alpha": alpha, "beta": beta, "gamma": gamma, "Xq": Xq,
+            "x_scale": s, "acc": acc, "Y": Y}

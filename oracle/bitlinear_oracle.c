@@ -45,6 +45,20 @@
  *      ([bitnet.cpp] "3. BitLinear operation": the product is multiplied by the
  *      weight scale and by the activation dequantization factor; no bias, [b1.58]
  *      "Proposed method").
+ *
+ * The 1-bit sign variant (the original BitNet that [bitnet.cpp] "1. Weight
+ * binarization" describes), same activations and rescale:
+ *   S1. alpha = mean(W): exact signed sum rounded once to fp64, alpha = sum / (N*K)
+ *       in fp64 ([bitnet.cpp] "1. Weight binarization": the weights are centred on
+ *       their mean).
+ *   S2. c = Sign(w - alpha) with Sign(x) = +1 for x > 0 and -1 otherwise, so a weight
+ *       equal to alpha gets -1 ([bitnet.cpp] the definition under "1. Weight
+ *       binarization"; [BitDelta] Eq. (2) is the same rule). The sign of w - alpha is
+ *       taken exactly: fp64(w) > alpha.
+ *   S3. beta = fp32(mean |W|), the scale of step 1 ([BitDelta] Eq. (3)-(4): mean |W|
+ *       is the scale that minimizes the L2 error of a sign code).
+ *   S4. eight codes per byte: code k = 8j+i in bit i of byte j, 1 for +1, 0 for -1.
+ *   S5. acc = sum_k Xq[t,k] * c[o,k] in integers; Y = fp32(acc * beta / s_t) in fp64.
  */
 #include <float.h>
 #include <math.h>
@@ -401,6 +415,105 @@ int orc_forward(const int8_t* Xq, const float* s, int64_t T, int64_t K, const ui
   int32_t* a = acc ? acc : (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * N));
   if (!a) return ORC_NOMEM;
   int st = orc_product(Xq, P, T, N, K, a);
+  if (!st) st = orc_rescale(a, s, beta, T, N, Y);
+  if (!acc) free(a);
+  return st;
+}
+
+/* ---------------------------------------------------------------- sign variant */
+
+static double term_id(const float* b, int64_t i) { return (double)b[i]; }
+
+/* Exact sum of n fp32 values (signed), rounded once to fp64. */
+int orc_sum(const float* w, int64_t n, double* out) {
+  if (n < 0) return ORC_DIM;
+  return exact_sum(w, n, term_id, out);
+}
+
+/* S2: c = +1 where fp64(w) > alpha, else -1. */
+int orc_sign_codes(const float* W, int64_t n, double alpha, int8_t* c) {
+  if (n < 0) return ORC_DIM;
+  for (int64_t i = 0; i < n; ++i) {
+    if (!isfinite(W[i])) return ORC_NONFINITE;
+    c[i] = ((double)W[i] > alpha) ? (int8_t)1 : (int8_t)-1;
+  }
+  return ORC_OK;
+}
+
+/* S1-S3 for W [N, K]: codes c [N, K], alpha (fp64), gamma = mean|W| (fp64), beta. */
+int orc_sign_weights(const float* W, int64_t N, int64_t K, int8_t* c, double* alpha,
+                     double* gamma, float* beta) {
+  if (N <= 0 || K <= 0) return ORC_DIM;
+  double sum;
+  int st = orc_sum(W, N * K, &sum);
+  if (st) return st;
+  const double a = sum / (double)(N * K);
+  st = orc_weight_scale(W, N, K, gamma, beta);
+  if (st) return st;
+  *alpha = a;
+  return orc_sign_codes(W, N * K, a, c);
+}
+
+/* S4: pack codes c [N, K] (K % 8 == 0) into P [N, K/8]. */
+int orc_pack1(const int8_t* c, int64_t N, int64_t K, uint8_t* P) {
+  if (N <= 0 || K <= 0 || K % 8) return ORC_DIM;
+  const int64_t nb = K / 8;
+  for (int64_t o = 0; o < N; ++o)
+    for (int64_t j = 0; j < nb; ++j) {
+      unsigned byte = 0u;
+      for (int i = 0; i < 8; ++i) {
+        const int8_t v = c[o * K + 8 * j + i];
+        if (v != 1 && v != -1) return ORC_BADCODE;
+        if (v == 1) byte |= 1u << i;
+      }
+      P[o * nb + j] = (uint8_t)byte;
+    }
+  return ORC_OK;
+}
+
+int orc_unpack1(const uint8_t* P, int64_t N, int64_t K, int8_t* c) {
+  if (N <= 0 || K <= 0 || K % 8) return ORC_DIM;
+  const int64_t nb = K / 8;
+  for (int64_t o = 0; o < N; ++o)
+    for (int64_t k = 0; k < K; ++k)
+      c[o * K + k] = ((P[o * nb + k / 8] >> (k % 8)) & 1u) ? (int8_t)1 : (int8_t)-1;
+  return ORC_OK;
+}
+
+/* S5, integer part: acc [T, N] = Xq [T, K] times the sign codes of P [N, K/8]. */
+int orc_product_sign(const int8_t* Xq, const uint8_t* P, int64_t T, int64_t N, int64_t K,
+                     int32_t* acc) {
+  if (T <= 0 || N <= 0 || K <= 0 || K % 8) return ORC_DIM;
+  const int64_t nb = K / 8;
+  int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t o = 0; o < N; ++o) {
+    const uint8_t* row = P + o * nb;
+    for (int64_t t = 0; t < T; ++t) {
+      const int8_t* x = Xq + t * K;
+      int64_t sum = 0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int c = ((row[k / 8] >> (k % 8)) & 1u) ? 1 : -1;
+        sum += (int64_t)x[k] * (int64_t)c;
+      }
+      if (sum > INT32_MAX || sum < INT32_MIN) {
+#pragma omp critical
+        status = ORC_OVERFLOW;
+        continue;
+      }
+      acc[t * N + o] = (int32_t)sum;
+    }
+  }
+  return status;
+}
+
+/* S5: Y = fp32(acc * beta / s_t) (the rescale of step 7). acc may be NULL. */
+int orc_forward_sign(const int8_t* Xq, const float* s, int64_t T, int64_t K, const uint8_t* P,
+                     float beta, int64_t N, float* Y, int32_t* acc) {
+  if (T <= 0 || N <= 0 || K <= 0 || K % 8) return ORC_DIM;
+  int32_t* a = acc ? acc : (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * N));
+  if (!a) return ORC_NOMEM;
+  int st = orc_product_sign(Xq, P, T, N, K, a);
   if (!st) st = orc_rescale(a, s, beta, T, N, Y);
   if (!acc) free(a);
   return st;

@@ -374,3 +374,132 @@ def test_forward_equals_dequantized_matmul():
     full = oracle.rmsnorm(X).astype(np.float64) @ W.astype(np.float64).T
     cos = np.sum(full * out["Y"]) / np.linalg.norm(full) / np.linalg.norm(out["Y"])
     assert abs(cos - corr) < 0.01
+
+
+# ---------------------------------------------------------------- 1-bit sign variant
+
+@pytest.mark.parametrize("seed", range(4))
+def test_signed_sum_equals_exact_rational(seed):
+    a = workloads.wide_range(2000, seed)
+    exact = sum((Fraction(float(v)) for v in a.astype(np.float64).ravel()), Fraction(0))
+    assert oracle.exact_sum(a) == float(exact)
+
+
+def test_signed_sum_cancellation():
+    # the large terms cancel exactly; what is left is far below their ulp
+    a = np.array([2.0 ** 100, 3.0, -(2.0 ** 100), 2.0 ** -60], np.float32)
+    assert oracle.exact_sum(a) == 3.0 + 2.0 ** -60
+    assert oracle.exact_sum(-a) == -(3.0 + 2.0 ** -60)
+
+
+def test_golden_sign_weights():
+    g = load("sign_weights.txt")
+    for k in ("A", "B"):
+        W = np.array(g[k + "_W"], np.float32)
+        c, alpha, gamma, beta = oracle.sign_weights(W)
+        assert alpha == g[k + "_alpha"] and beta == g[k + "_beta"]
+        assert c.tolist() == g[k + "_codes"]
+        assert oracle.pack1(c).tolist() == g[k + "_packed"]
+        assert oracle.unpack1(oracle.pack1(c), W.shape[1]).tolist() == g[k + "_codes"]
+
+
+def test_golden_sign_forward():
+    g = load("sign_weights.txt")
+    P = np.array(g["A_packed"], np.uint8)
+    Y, acc = oracle.forward_sign(np.array(g["C_Xq"], np.int8), np.array(g["C_s"], np.float32),
+                                 P, np.float32(g["A_beta"]))
+    assert acc.tolist() == g["C_acc"] and Y.tolist() == g["C_Y"]
+
+
+def test_sign_alpha_is_exact_mean_and_codes_threshold():
+    r = np.random.default_rng(3)
+    W = (r.standard_normal((37, 64)) * 0.02 + 0.003).astype(np.float32)
+    c, alpha, gamma, beta = oracle.sign_weights(W)
+    exact = sum((Fraction(float(v)) for v in W.astype(np.float64).ravel()), Fraction(0))
+    assert alpha == float(exact) / W.size  # the exact sum rounded once, then one division
+    # the code is the sign of the exact difference, -1 on a tie
+    w64 = W.astype(np.float64)
+    assert np.array_equal(c, np.where(w64 > alpha, 1, -1).astype(np.int8))
+    # a weight placed exactly on alpha goes to -1, one ulp above goes to +1
+    W2 = np.array([[1.0, 2.0, 3.0, 4.0, 2.5, 2.5, 2.5, 2.5]], np.float32)  # mean 2.5
+    c2, a2, _, _ = oracle.sign_weights(W2)
+    assert a2 == 2.5 and c2.tolist() == [[-1, -1, 1, 1, -1, -1, -1, -1]]
+    W3 = W2.copy()
+    W3[0, 4] = np.nextafter(np.float32(2.5), np.float32(3.0))
+    c3, a3, _, _ = oracle.sign_weights(W3)
+    # sum = 20 + 2^-22 (one fp32 ulp of 2.5), alpha = 2.5 + 2^-25 < 2.5 + 2^-22
+    assert a3 == 2.5 + 2.0 ** -25
+    assert c3.tolist() == [[-1, -1, 1, 1, 1, -1, -1, -1]]
+
+
+def test_sign_codes_invariants_gaussian():
+    # codes are +-1 only; about half are +1 for a symmetric distribution about its mean;
+    # beta = mean |W| -> sigma * sqrt(2/pi) for zero-mean Gaussian weights
+    r = np.random.default_rng(11)
+    W = (r.standard_normal((512, 2048)) * 0.02).astype(np.float32)
+    c, alpha, gamma, beta = oracle.sign_weights(W)
+    assert set(np.unique(c).tolist()) <= {-1, 1}
+    assert abs(float((c == 1).mean()) - 0.5) < 0.003
+    assert abs(gamma / (0.02 * math.sqrt(2.0 / math.pi)) - 1.0) < 0.003
+    assert beta == F32(gamma)
+
+
+def test_sign_scale_minimizes_l2_error():
+    # [BitDelta] Eq. (3)-(4): for a sign code S = Sign(W) the error ||W - b S||^2 is
+    # smallest at b = mean |W|. Zero-mean W (each value with its negative) makes
+    # alpha = 0, so the oracle's codes are Sign(W) itself.
+    r = np.random.default_rng(5)
+    half = (r.standard_normal(4096) * 0.02).astype(np.float32)
+    W = np.concatenate([half, -half]).reshape(8, 1024)
+    c, alpha, gamma, beta = oracle.sign_weights(W)
+    assert alpha == 0.0
+    w = W.astype(np.float64).ravel()
+    s = c.astype(np.float64).ravel()
+
+    def err(b):
+        return float(np.sum((w - b * s) ** 2))
+
+    e0 = err(gamma)
+    for d in (1e-3, 1e-5, 1e-7):
+        assert e0 <= err(gamma * (1 + d)) and e0 <= err(gamma * (1 - d))
+    # the closed-form minimizer sum(W*S)/sum(S*S) equals mean |W|
+    assert abs(float(np.dot(w, s) / np.dot(s, s)) - gamma) <= 1e-12 * gamma
+
+
+def test_pack1_layout_roundtrip_and_density():
+    r = np.random.default_rng(2)
+    c = np.where(r.random((13, 64)) < 0.5, -1, 1).astype(np.int8)
+    P = oracle.pack1(c)
+    assert P.shape == (13, 8)
+    for o in range(13):
+        for k in range(64):
+            assert ((int(P[o, k // 8]) >> (k % 8)) & 1) == (1 if c[o, k] == 1 else 0)
+    assert np.array_equal(oracle.unpack1(P, 64), c)
+    with pytest.raises(oracle.OracleError):
+        oracle.pack1(np.zeros((1, 8), np.int8))  # 0 is not a sign code
+    # one bit per weight: an 8B-parameter model packs into 1e9 bytes
+    assert 8_000_000_000 // 8 == 1_000_000_000
+
+
+def test_sign_product_bruteforce_and_identity():
+    r = np.random.default_rng(9)
+    T, N, K = 3, 7, 96
+    Xq = r.integers(-128, 128, (T, K), dtype=np.int64).astype(np.int8)
+    c = np.where(r.random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    acc = oracle.product_sign(Xq, oracle.pack1(c), K)
+    for t in range(T):
+        for o in range(N):
+            assert int(acc[t, o]) == sum(int(Xq[t, k]) * int(c[o, k]) for k in range(K))
+    # sum c*x = 2 * sum_{c=+1} x - sum x
+    pos = (c == 1).astype(np.int64)
+    assert np.array_equal(acc, 2 * (Xq.astype(np.int64) @ pos.T) - Xq.astype(np.int64).sum(1)[:, None])
+
+
+def test_sign_forward_equals_dequantized_matmul():
+    r = np.random.default_rng(4)
+    X = r.standard_normal((5, 256)).astype(np.float32)
+    W = (r.standard_normal((33, 256)) * 0.02).astype(np.float32)
+    out = oracle.bitlinear_sign(X, W)
+    deq = (out["Xq"].astype(np.float64) / out["x_scale"].astype(np.float64)[:, None]) @ \
+          (out["codes"].astype(np.float64) * float(out["beta"])).T
+    assert np.allclose(out["Y"].astype(np.float64), deq, rtol=1e-6, atol=1e-6 * np.abs(deq).max())

@@ -188,6 +188,40 @@ typedef struct bl_proj_desc {
 bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_t T,
                                     bl_stream_t stream);
 
+/* ---------------------------------------------------------------- 1-bit sign variant
+ *
+ * The original BitNet weight binarization ([bitnet.cpp] "1. Weight binarization":
+ * W_f = Sign(W - alpha) with alpha the mean of W and Sign(x) = +1 for x > 0, -1
+ * otherwise; [BitDelta] Eq. (2) is the same rule and Eq. (4) gives mean |W| as the
+ * scale of a sign code). Activations are quantized by bitlinear_quantize_acts; the
+ * rescale is that of bitlinear_forward. Computes:
+ *   alpha = (exact sum of W, rounded once to fp64) / (N*K) in fp64
+ *   c     = +1 where fp64(w) > alpha, else -1 (an exact comparison)
+ *   beta  = fp32(mean |W|), as in bitlinear_quantize_weights
+ *   bits  = bit i of byte j of row o holds code k = 8j+i, 1 for +1 and 0 for -1
+ * Arguments:
+ *   W          device fp32 [N, K], K % 8 == 0, 16-byte aligned; read only
+ *   W_bits     device uint8 [N, K/8], 16-byte aligned; written
+ *   w_scale    device fp32 [1]; receives beta
+ *   w_alpha    device fp64 [1] or NULL; receives alpha
+ *   workspace  as for bitlinear_quantize_weights (the same size covers both) */
+bl_status bitlinear_quantize_weights_sign(const float* W, int64_t N, int64_t K,
+                                          uint8_t* W_bits, float* w_scale, double* w_alpha,
+                                          void* workspace, size_t workspace_bytes,
+                                          bl_stream_t stream);
+
+/* acc[t, o] = sum_k Xq[t, k] * c[o, k] (exact, int32), Y = fp32(acc) * fp32(beta / s_t).
+ * W_bits uint8 [N, K/8] from bitlinear_quantize_weights_sign, K % 8 == 0. T == 1 with
+ * K % 128 == 0 runs the decode GEMV, any other shape a one-thread-per-output kernel. */
+bl_status bitlinear_forward_sign(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                                 const uint8_t* W_bits, const float* w_scale, int64_t N,
+                                 float* Y, int32_t* acc, bl_stream_t stream);
+
+/* bitlinear_forward_sign over `count` (1..BL_MAX_GROUP) projections (W_packed of each
+ * entry holds sign bits, [N, K/8]); one launch per kernel kind. */
+bl_status bitlinear_forward_sign_grouped(const bl_proj_desc* descs, int count, int64_t T,
+                                         bl_stream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* bitlinear_status_str(bl_status s);
 /* Text of the last failing HIP call made by this thread ("" if none). */

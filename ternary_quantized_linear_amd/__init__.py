@@ -74,6 +74,11 @@ _c_fwx = _sig("bitlinear_forward_ex",
               [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_int, _P])
 _c_choice = _sig("bitlinear_forward_choice", [_I64, _I64, _I64])
 _c_fwg = _sig("bitlinear_forward_grouped", [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
+_c_qws = _sig("bitlinear_quantize_weights_sign",
+              [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P])
+_c_fws = _sig("bitlinear_forward_sign", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P])
+_c_fwsg = _sig("bitlinear_forward_sign_grouped",
+               [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
 _c_str = _sig("bitlinear_status_str", [ctypes.c_int], ctypes.c_char_p)
 _c_err = _sig("bitlinear_last_hip_error", [], ctypes.c_char_p)
 _c_ver = _sig("bitlinear_abi_version", [])
@@ -175,6 +180,35 @@ def bitlinear_forward_grouped(entries, T, stream=None):
            "bitlinear_forward_grouped")
 
 
+def bitlinear_quantize_weights_sign(W, W_bits, w_scale, w_alpha, workspace, stream=None):
+    N, K = W.shape
+    _check(_c_qws(_ptr(W), N, K, _ptr(W_bits), _ptr(w_scale), _ptr(w_alpha), _ptr(workspace),
+                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                  _stream(W, stream)), "bitlinear_quantize_weights_sign")
+
+
+def bitlinear_forward_sign(Xq, x_scale, W_bits, w_scale, Y, acc=None, stream=None):
+    T, K = Xq.shape
+    N = W_bits.shape[0]
+    _check(_c_fws(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_bits), _ptr(w_scale), N, _ptr(Y),
+                  _ptr(acc), _stream(Xq, stream)), "bitlinear_forward_sign")
+
+
+def _proj_array(entries):
+    arr = (_ProjDesc * len(entries))()
+    for i, (Xq, xs, Wp, ws, Y, acc) in enumerate(entries):
+        arr[i] = _ProjDesc(Xq.data_ptr(), xs.data_ptr(), Wp.data_ptr(), ws.data_ptr(),
+                           Y.data_ptr(), None if acc is None else acc.data_ptr(),
+                           Wp.shape[0], Xq.shape[-1])
+    return arr
+
+
+def bitlinear_forward_sign_grouped(entries, T, stream=None):
+    """entries: list of (Xq, x_scale, W_bits, w_scale, Y, acc_or_None)."""
+    _check(_c_fwsg(_proj_array(entries), len(entries), T, _stream(entries[0][0], stream)),
+           "bitlinear_forward_sign_grouped")
+
+
 class PreparedCall:
     """A grouped ABI call with its descriptor array marshalled once. Calling it
     launches on the current stream at call time (so it can be captured into a graph)."""
@@ -208,6 +242,12 @@ def prepare_forward_grouped(entries, T):
     return PreparedCall(_c_fwg, arr, len(entries), T, (), "bitlinear_forward_grouped", keep)
 
 
+def prepare_forward_sign_grouped(entries, T):
+    keep = [t for e in entries for t in e if t is not None]
+    return PreparedCall(_c_fwsg, _proj_array(entries), len(entries), T, (),
+                        "bitlinear_forward_sign_grouped", keep)
+
+
 # ---------------------------------------------------------------- allocating wrappers
 
 def quantize_weights(W: torch.Tensor, with_gamma: bool = False):
@@ -220,6 +260,29 @@ def quantize_weights(W: torch.Tensor, with_gamma: bool = False):
     ws = torch.empty(bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
     bitlinear_quantize_weights(W, packed, beta, gamma, ws)
     return (packed, beta, gamma) if with_gamma else (packed, beta)
+
+
+def quantize_weights_sign(W: torch.Tensor):
+    """W fp32 [N, K] (K % 8 == 0) on the GPU -> (sign bits uint8 [N, K/8], beta fp32 [1],
+    alpha fp64 [1])."""
+    N, K = W.shape
+    dev = W.device
+    bits = torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    alpha = torch.empty(1, dtype=torch.float64, device=dev)
+    ws = torch.empty(bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    bitlinear_quantize_weights_sign(W, bits, beta, alpha, ws)
+    return bits, beta, alpha
+
+
+def forward_sign(Xq, x_scale, bits, beta, with_acc: bool = False):
+    """(Xq [T, K], x_scale [T], sign bits [N, K/8], beta [1]) -> Y fp32 [T, N] (and acc)."""
+    T = Xq.shape[0]
+    N = bits.shape[0]
+    Y = torch.empty((T, N), dtype=torch.float32, device=Xq.device)
+    acc = torch.empty((T, N), dtype=torch.int32, device=Xq.device) if with_acc else None
+    bitlinear_forward_sign(Xq, x_scale, bits, beta, Y, acc)
+    return (Y, acc) if with_acc else Y
 
 
 def quantize_acts(X: torch.Tensor, gain=None, eps: float = 1e-6, flags: int = 0):

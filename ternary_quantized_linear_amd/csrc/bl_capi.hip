@@ -184,6 +184,56 @@ bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_
   return BL_OK;
 }
 
+bl_status bitlinear_quantize_weights_sign(const float* W, int64_t N, int64_t K, uint8_t* W_bits,
+                                          float* w_scale, double* w_alpha, void* workspace,
+                                          size_t workspace_bytes, bl_stream_t stream) {
+  if (!W || !W_bits || !w_scale) return BL_ERR_NULL;
+  if (N <= 0 || K <= 0 || K % 8 || N > kMaxRows || N * K > kMaxWeights) return BL_ERR_DIM;
+  if (!workspace || workspace_bytes < bitlinear_weight_workspace_bytes(N, K))
+    return BL_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(W_bits) || !aligned16(workspace) || !aligned_n(w_scale, 4) ||
+      (w_alpha && !aligned_n(w_alpha, 8)))
+    return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_quantize_weights_sign(W, N, K, W_bits, w_scale, w_alpha, workspace,
+                                                    (hipStream_t)stream));
+}
+
+bl_status bitlinear_forward_sign_grouped(const bl_proj_desc* descs, int count, int64_t T,
+                                         bl_stream_t stream) {
+  if (!descs) return BL_ERR_NULL;
+  if (count < 1 || count > BL_MAX_GROUP) return BL_ERR_ARG;
+  bl_proj_internal gemv[BL_MAX_GROUP];
+  int ng = 0;
+  for (int i = 0; i < count; ++i) {
+    const bl_proj_desc& d = descs[i];
+    bl_status s = check_proj(d.Xq, d.x_scale, T, d.K, d.W_packed, d.w_scale, d.N, d.Y, d.acc);
+    if (s != BL_OK) return s;
+    if (d.K % 8) return BL_ERR_DIM;
+  }
+  (void)hipGetLastError();
+  for (int i = 0; i < count; ++i) {
+    const bl_proj_desc& d = descs[i];
+    const bl_proj_internal p = to_internal(d.Xq, d.x_scale, d.K, d.W_packed, d.w_scale, d.N, d.Y,
+                                           d.acc);
+    if (bl_gemv_sign_supports((int)T, (int)d.K)) {
+      gemv[ng++] = p;
+    } else {
+      bl_status s = hip_status(bl_launch_generic_sign(&p, (int)T, (hipStream_t)stream));
+      if (s != BL_OK) return s;
+    }
+  }
+  if (ng > 0) return hip_status(bl_launch_gemv_sign(gemv, ng, (hipStream_t)stream));
+  return BL_OK;
+}
+
+bl_status bitlinear_forward_sign(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                                 const uint8_t* W_bits, const float* w_scale, int64_t N,
+                                 float* Y, int32_t* acc, bl_stream_t stream) {
+  const bl_proj_desc d{Xq, x_scale, W_bits, w_scale, Y, acc, N, K};
+  return bitlinear_forward_sign_grouped(&d, 1, T, stream);
+}
+
 const char* bitlinear_status_str(bl_status s) {
   switch (s) {
     case BL_OK: return "ok";

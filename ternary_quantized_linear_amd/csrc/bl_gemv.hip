@@ -35,6 +35,14 @@
 //     a03 + a1/4 + a2/16 (exact shifts of exact multiples) started at minus the lane's
 //     own activation sum: sum x*q exactly.
 //   - Lane sums are reduced with DPP; Y = fp32(acc) * fp32(beta / s).
+//
+// The same kernel serves the 1-bit sign variant ([bitnet.cpp] "1. Weight
+// binarization": codes +-1, eight per byte, bit i of byte j = code 8j+i set for +1).
+// A 16-byte chunk then holds 128 codes; the lane keeps its 128 activations as eight
+// "bit planes" per packed dword (plane i, byte b = activation of code 8b+i). Planes 0..6
+// are masked in place (values 2^i * bit, all below 128) into their own dot4
+// accumulator, plane 7 is shifted down and shares plane 0's; sum_i a_i / 2^i is the
+// sum of the activations whose code is +1, P, and sum c*x = 2P - sum x.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -110,6 +118,58 @@ __device__ __forceinline__ int acc_total(const Acc4& s) {
   return s.a0 + (s.a1 >> 2) + (s.a2 >> 4);
 }
 
+// 1-bit: accumulator i carries plane i times 2^i (plane 7 rides on accumulator 0).
+struct Acc8 {
+  int a[7];
+};
+
+__device__ __forceinline__ void dot_word1(uint32_t w, const uint32_t (&x)[8], Acc8& s) {
+  s.a[0] = sdot4(w & 0x01010101u, x[0], s.a[0]);
+  s.a[1] = sdot4(w & 0x02020202u, x[1], s.a[1]);
+  s.a[2] = sdot4(w & 0x04040404u, x[2], s.a[2]);
+  s.a[3] = sdot4(w & 0x08080808u, x[3], s.a[3]);
+  s.a[4] = sdot4(w & 0x10101010u, x[4], s.a[4]);
+  s.a[5] = sdot4(w & 0x20202020u, x[5], s.a[5]);
+  s.a[6] = sdot4(w & 0x40404040u, x[6], s.a[6]);
+  s.a[0] = sdot4((w >> 7) & 0x01010101u, x[7], s.a[0]);
+}
+
+// sum over the lane's codes of c * x, from the plane sums and the lane's activation sum
+__device__ __forceinline__ int acc1_total(const Acc8& s, int xsum) {
+  const int pos = s.a[0] + (s.a[1] >> 1) + (s.a[2] >> 2) + (s.a[3] >> 3) + (s.a[4] >> 4) +
+                  (s.a[5] >> 5) + (s.a[6] >> 6);
+  return 2 * pos - xsum;
+}
+
+// Activations of 1-bit chunk c (128 codes) as 4 x 8 bit planes, and their sum.
+__device__ __forceinline__ void load_act_chunk1(const int8_t* x, int c, bool on,
+                                                uint32_t (&o)[4][8], int& xsum) {
+  const uint4* src = reinterpret_cast<const uint4*>(x + 128 * c);
+  uint32_t raw[32];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint4 v = src[d];
+    if (!on) v = make_uint4(0u, 0u, 0u, 0u);
+    raw[4 * d] = v.x;
+    raw[4 * d + 1] = v.y;
+    raw[4 * d + 2] = v.z;
+    raw[4 * d + 3] = v.w;
+    xsum += byte_sum(v.x) + byte_sum(v.y) + byte_sum(v.z) + byte_sum(v.w);
+  }
+  // packed dword j covers codes 32j..32j+31; plane i byte b = x[32j + 8b + i], which is
+  // byte i % 4 of raw dword 8j + 2b + i / 4
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int h = i >> 2, q = i & 3;
+      const uint32_t sel = 0x0C0C0000u | (uint32_t)(4 + q) << 8 | (uint32_t)q;  // lo: b0, b1
+      const uint32_t lo = __builtin_amdgcn_perm(raw[8 * j + 2 + h], raw[8 * j + h], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(raw[8 * j + 6 + h], raw[8 * j + 4 + h], sel);
+      o[j][i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+}
+
 // Activations of chunk c (64 codes): 4 x 16 bytes, transposed, and their sum; zeros when
 // the lane has no chunk.
 __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, uint4 (&o)[4],
@@ -130,7 +190,7 @@ __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, 
 // One projection's partition. L lanes per row, I chunks per lane, S waves per row
 // (S > 1 needs L = 64). Wave `wave` of partition workgroup `wgl` takes segment wave % S
 // of row groups wgl * (4/S) + wave / S + k * stride, k = 0, 1, ...
-template <int L, int I, int S>
+template <int L, int I, int S, int FMT>
 __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
                                       unsigned long long* slots) {
   constexpr int RW = kWave / L;        // rows per row group
@@ -188,10 +248,15 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   uint4 w[kGemvDepth][I];
 #pragma unroll
   for (int d = 0; d < kGemvDepth; ++d) load_w(w[d]);
-  uint4 x[I][4];
+  // activations: 2-bit chunks as 4 transposed uint4, 1-bit chunks as 4 x 8 bit planes
+  uint4 x[FMT == 0 ? I : 1][4];
+  uint32_t x1[FMT == 1 ? I : 1][4][8];
   int xsum = 0;
 #pragma unroll
-  for (int i = 0; i < I; ++i) load_act_chunk(P.Xq, ci[i], on[i], x[i], xsum);
+  for (int i = 0; i < I; ++i) {
+    if constexpr (FMT == 0) load_act_chunk(P.Xq, ci[i], on[i], x[i], xsum);
+    else load_act_chunk1(P.Xq, ci[i], on[i], x1[i], xsum);
+  }
   typedef const float __attribute__((address_space(4)))* ConstF;
   const float f = *(ConstF)P.ws / *(ConstF)P.xs;
   int g = g0, k = 0;
@@ -212,11 +277,25 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   };
   // one row group: consume buffer d, refill it D groups ahead (prefetch), keep the total
   auto step = [&](int d, bool prefetch) {
-    Acc4 s{-xsum, 0, 0};
+    int lane_tot;
+    if constexpr (FMT == 0) {
+      Acc4 s{-xsum, 0, 0};
 #pragma unroll
-    for (int i = 0; i < I; ++i) dot_chunk(w[d][i], x[i], s);
+      for (int i = 0; i < I; ++i) dot_chunk(w[d][i], x[i], s);
+      lane_tot = acc_total(s);
+    } else {
+      Acc8 s{{0, 0, 0, 0, 0, 0, 0}};
+#pragma unroll
+      for (int i = 0; i < I; ++i) {
+        dot_word1(w[d][i].x, x1[i][0], s);
+        dot_word1(w[d][i].y, x1[i][1], s);
+        dot_word1(w[d][i].z, x1[i][2], s);
+        dot_word1(w[d][i].w, x1[i][3], s);
+      }
+      lane_tot = acc1_total(s, xsum);
+    }
     if (prefetch) load_w(w[d]);
-    int tot = group_sum_to_last<L>(acc_total(s));
+    int tot = group_sum_to_last<L>(lane_tot);
     if constexpr (S > 1) {
       // the S segment sums of this row meet in one LDS word; the wave that completes
       // the count holds the row total
@@ -262,7 +341,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
 
 // MAXI = 2 adds the mapping for rows of more than 256 chunks (two chunks per lane);
 // the MAXI = 1 instance leaves it out so that its register budget stays small.
-template <int MAXI>
+template <int MAXI, int FMT>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
   extern __shared__ unsigned long long slots[];
   const ArgsPtr a = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
@@ -281,13 +360,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
     __syncthreads();
   }
   switch (P.cfg) {
-    case 0: sweep<16, 1, 1>(P, wgl, wave, slots); break;  // C <= 16
-    case 1: sweep<32, 1, 1>(P, wgl, wave, slots); break;  // C <= 32
-    case 2: sweep<64, 1, 1>(P, wgl, wave, slots); break;  // C <= 64
-    case 3: sweep<64, 1, 2>(P, wgl, wave, slots); break;  // C <= 128
-    case 4: sweep<64, 1, 4>(P, wgl, wave, slots); break;  // C <= 256
+    case 0: sweep<16, 1, 1, FMT>(P, wgl, wave, slots); break;  // C <= 16
+    case 1: sweep<32, 1, 1, FMT>(P, wgl, wave, slots); break;  // C <= 32
+    case 2: sweep<64, 1, 1, FMT>(P, wgl, wave, slots); break;  // C <= 64
+    case 3: sweep<64, 1, 2, FMT>(P, wgl, wave, slots); break;  // C <= 128
+    case 4: sweep<64, 1, 4, FMT>(P, wgl, wave, slots); break;  // C <= 256
     default:
-      if constexpr (MAXI >= 2) sweep<64, 2, 4>(P, wgl, wave, slots);  // C <= 512
+      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT>(P, wgl, wave, slots);  // C <= 512
       break;
   }
 }
@@ -307,6 +386,7 @@ GemvCfg gemv_cfg(int C) {
 
 // Workgroups of one instance the device keeps resident at once (queried once per
 // instance; the combine words never take enough LDS to change it).
+template <int FMT>
 int gemv_resident(bool big, size_t lds) {
   static int cached[2] = {0, 0};
   if (cached[big]) return cached[big];
@@ -318,7 +398,7 @@ int gemv_resident(bool big, size_t lds) {
       cus = 256;
   }
   int per = 0;
-  const void* f = big ? (const void*)gemv_kernel<2> : (const void*)gemv_kernel<1>;
+  const void* f = big ? (const void*)gemv_kernel<2, FMT> : (const void*)gemv_kernel<1, FMT>;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, kGemvThreads, lds) != hipSuccess ||
       per < 1)
     per = 2;
@@ -331,6 +411,9 @@ int gemv_resident(bool big, size_t lds) {
 using namespace bl;
 
 bool bl_gemv_supports(int T, int K) { return T == 1 && K % 64 == 0 && K / 64 <= kGemvMaxC; }
+bool bl_gemv_sign_supports(int T, int K) {
+  return T == 1 && K % 128 == 0 && K / 128 <= kGemvMaxC;
+}
 
 // Relative cost of a byte streamed by segmented rows (S waves meet per row in LDS and
 // an eighth of a segment's lanes may idle) against a byte of a one-wave row, in 1/16.
@@ -338,8 +421,10 @@ bool bl_gemv_supports(int T, int K) { return T == 1 && K % 64 == 0 && K / 64 <= 
 #define BL_GEMV_SEG_COST16 20
 #endif
 
-hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
-  (void)T;
+namespace {
+template <int FMT>
+hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t stream) {
+  constexpr int kCodes = FMT == 0 ? 64 : 128;  // codes per 16-byte chunk
   GemvArgs a{};
   int64_t total = 0;
   GemvCfg cfg[BL_GROUP_CAP];
@@ -347,9 +432,9 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
   int order[BL_GROUP_CAP];
   bool big = false;
   for (int i = 0; i < count; ++i) {
-    cfg[i] = gemv_cfg((int)(p[i].K / 64));
+    cfg[i] = gemv_cfg((int)(p[i].K / kCodes));
     big = big || cfg[i].cfg == 5;
-    const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
+    const int64_t bytes = (int64_t)p[i].N * (p[i].K / kCodes) * 16;
     cost[i] = cfg[i].S > 1 ? bytes * BL_GEMV_SEG_COST16 / 16 : bytes;
     total += cost[i];
     order[i] = i;
@@ -365,7 +450,7 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
   // One round of resident workgroups (the combine words take at most a few KB of LDS);
   // each projection gets workgroups in proportion to its cost, at least one and never
   // one without a row group.
-  const int cap = gemv_resident(big, 4096);
+  const int cap = gemv_resident<FMT>(big, 4096);
   int wgs = 0, slots = 0;
   for (int o = 0; o < count; ++o) {
     const int i = order[o];
@@ -378,7 +463,7 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
     g.Y = p[i].Y;
     g.acc = p[i].acc;
     g.N = (int)p[i].N;
-    g.C = (int)(p[i].K / 64);
+    g.C = (int)(p[i].K / kCodes);
     g.cfg = c.cfg;
     g.CW = (g.C + c.S - 1) / c.S;
     const int groups = (g.N + c.RW - 1) / c.RW;
@@ -402,8 +487,20 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
   a.slots = slots;
   const size_t lds = sizeof(unsigned long long) * (size_t)slots;
   if (big)
-    hipLaunchKernelGGL(gemv_kernel<2>, dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream, a);
+    hipLaunchKernelGGL((gemv_kernel<2, FMT>), dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream,
+                       a);
   else
-    hipLaunchKernelGGL(gemv_kernel<1>, dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream, a);
+    hipLaunchKernelGGL((gemv_kernel<1, FMT>), dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream,
+                       a);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
+  (void)T;
+  return launch_gemv_fmt<0>(p, count, stream);
+}
+
+hipError_t bl_launch_gemv_sign(const bl_proj_internal* p, int count, hipStream_t stream) {
+  return launch_gemv_fmt<1>(p, count, stream);
 }

@@ -35,3 +35,11 @@ hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStre
 bool bl_prefill_supports(int T, int K);
 hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream);
 hipError_t bl_launch_generic(const bl_proj_internal* p, int T, hipStream_t stream);
+
+// The 1-bit sign variant: weights 8 codes per byte (N rows of K/8 bytes).
+hipError_t bl_launch_quantize_weights_sign(const float* W, int64_t N, int64_t K, uint8_t* P,
+                                           float* w_scale, double* w_alpha, void* ws,
+                                           hipStream_t stream);
+bool bl_gemv_sign_supports(int T, int K);
+hipError_t bl_launch_gemv_sign(const bl_proj_internal* p, int count, hipStream_t stream);
+hipError_t bl_launch_generic_sign(const bl_proj_internal* p, int T, hipStream_t stream);

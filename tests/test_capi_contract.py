@@ -51,7 +51,8 @@ def test_header_declares_the_abi():
               "bitlinear_forward_ex", "bitlinear_forward_grouped",
               "bitlinear_quantize_acts_grouped", "bitlinear_weight_workspace_bytes",
               "bitlinear_status_str", "bitlinear_last_hip_error", "bitlinear_abi_version",
-              "bitlinear_forward_choice"]:
+              "bitlinear_forward_choice", "bitlinear_quantize_weights_sign",
+              "bitlinear_forward_sign", "bitlinear_forward_sign_grouped"]:
         assert n in names
 
 
@@ -214,3 +215,33 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def test_sign_variant_validation(lib):
+    f = lib.bitlinear_quantize_weights_sign
+    f.argtypes = [P, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+    f.restype = ctypes.c_int
+    lib.bitlinear_weight_workspace_bytes.argtypes = [I64, I64]
+    lib.bitlinear_weight_workspace_bytes.restype = ctypes.c_size_t
+    ws = lib.bitlinear_weight_workspace_bytes(256, 1024)
+    assert f(None, 256, 1024, B, C, None, D, ws, None) == BL_ERR_NULL
+    assert f(A, 256, 1024, None, C, None, D, ws, None) == BL_ERR_NULL
+    assert f(A, 256, 1020, B, C, None, D, ws, None) == BL_ERR_DIM  # K % 8
+    assert f(A, 256, 1024, B, C, None, D, ws - 1, None) == BL_ERR_WORKSPACE
+    assert f(A, 256, 1024, MIS, C, None, D, ws, None) == BL_ERR_ALIGN
+    assert f(A, 256, 1024, B, C, P(0x300004), D, ws, None) == BL_ERR_ALIGN  # alpha
+    g = lib.bitlinear_forward_sign
+    g.argtypes = [P, P, I64, I64, P, P, I64, P, P, P]
+    g.restype = ctypes.c_int
+    assert g(None, B, 1, 4096, C, D, 4096, E, None, None) == BL_ERR_NULL
+    assert g(A, B, 1, 4100, C, D, 4096, E, None, None) == BL_ERR_DIM  # K % 8
+    assert g(A, B, 1, 4096, C, D, 4096, MIS, None, None) == BL_ERR_ALIGN
+    fg = lib.bitlinear_forward_sign_grouped
+    fg.argtypes = [ctypes.POINTER(ProjDesc), ctypes.c_int, I64, P]
+    fg.restype = ctypes.c_int
+    pa = (ProjDesc * 9)(*[ProjDesc(A.value, B.value, C.value, D.value, E.value, None, 64, 1024)
+                          for _ in range(9)])
+    assert fg(None, 1, 1, None) == BL_ERR_NULL
+    assert fg(pa, 9, 1, None) == BL_ERR_ARG
+    pa[1].K = 1028
+    assert fg(pa, 2, 1, None) == BL_ERR_DIM

@@ -330,6 +330,77 @@ def run_weight_quant(torch, bl, workloads):
     return res
 
 
+def run_sign_decode(torch, bl, workloads, T=1):
+    """The 1-bit sign variant on the decode8b layer: grouped act-quant + grouped sign GEMV
+    (eight codes per byte), rotating replicas, graph-replayed; and the sign quantizer on
+    the 70B down matrix."""
+    dev = torch.device("cuda:0")
+    Ws = workloads.decode8b_layer(0)
+    base = {n: bl.quantize_weights_sign(torch.from_numpy(W).to(dev))[:2] for n, W in Ws.items()}
+    reps = [base] + [{n: (b.clone(), s.clone()) for n, (b, s) in base.items()}
+                     for _ in range(REPLICAS - 1)]
+    inputs = workloads.decode8b_inputs(T, 100)
+    acts, act_entries = {}, []
+    for name, X in inputs.items():
+        Xq = torch.empty(X.shape, dtype=torch.int8, device=dev)
+        xs = torch.empty(T, dtype=torch.float32, device=dev)
+        acts[name] = (Xq, xs)
+        act_entries.append((torch.from_numpy(X).to(dev), None, Xq, xs))
+    qa = bl.prepare_quantize_acts_grouped(act_entries, T)
+    outs = {p: torch.empty((T, N), dtype=torch.float32, device=dev)
+            for p, (N, K) in workloads.LLAMA3_8B.items()}
+    fws = []
+    for r in reps:
+        entries = []
+        for name, projs in workloads.LLAMA3_8B_INPUTS.items():
+            Xq, xs = acts[name]
+            for p in projs:
+                bits, b = r[p]
+                entries.append((Xq, xs, bits, b, outs[p], None))
+        fws.append(bl.prepare_forward_sign_grouped(entries, T))
+    n_k = 256
+    g_k = _warm_then_capture(torch, [fws[i % len(fws)] for i in range(n_k)])
+    g_k.replay()
+    ms_gemv = _time_graph(torch, g_k, 2) / n_k
+    steps = 256
+    fns = []
+    for i in range(steps):
+        fns += [qa, fws[i % len(fws)]]
+    g_s = _warm_then_capture(torch, fns)
+    g_s.replay()
+    ms_step = _time_graph(torch, g_s, 1) / steps
+    gemv_b = sum(N * K // 8 + T * K + 4 * T + 4 + 4 * T * N
+                 for (N, K) in workloads.LLAMA3_8B.values())
+    act_b = sum(act_bytes(T, workloads.LLAMA3_8B[ps[0]][1])
+                for ps in workloads.LLAMA3_8B_INPUTS.values())
+    del reps, base
+    # sign quantizer on the 70B down matrix (exact signed sum + exact |W| sum + bits)
+    N, K = workloads.LLAMA_70B_SWEEP["down"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * workloads.WEIGHT_SIGMA
+    bits = torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    alpha = torch.empty(1, dtype=torch.float64, device=dev)
+    ws = torch.empty(bl.bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    g_w = _warm_then_capture(torch, [lambda: bl.bitlinear_quantize_weights_sign(
+        W, bits, beta, alpha, ws)] * 8)
+    g_w.replay()
+    ms_wq = _time_graph(torch, g_w, 1) / 8
+    wq_bytes = N * K * 4 + N * K // 8
+    del W, bits, ws
+    torch.cuda.empty_cache()
+    return {"workload": "decode8b layer, 1-bit sign weights (27.3 MB)",
+            "kernel": "gemv_kernel<1, 1> (grouped, 7 projections)",
+            "gemv_us": round(ms_gemv * 1e3, 3), "gemv_bytes": gemv_b,
+            "gemv_gbs": round(gemv_b / (ms_gemv * 1e-3) / 1e9, 1),
+            "gemv_frac_hbm": round(gemv_b / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_us": round(ms_step * 1e3, 3),
+            "step_gbs": round((gemv_b + act_b) / (ms_step * 1e-3) / 1e9, 1),
+            "quantize_weights_70b_down_ms": round(ms_wq, 4),
+            "quantize_weights_gbs_algorithmic": round(wq_bytes / (ms_wq * 1e-3) / 1e9, 1)}
+
+
 def run_calib_copy(torch):
     n = 64 * 1024 * 1024  # 256 MiB of fp32
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -446,6 +517,7 @@ def main():
         line["sweep70b"] = run_sweep70b(torch, bl, workloads)
         line["fullpass"] = run_fullpass(torch, bl, workloads)
         line["weight_quant"] = run_weight_quant(torch, bl, workloads)
+        line["sign_decode8b"] = run_sign_decode(torch, bl, workloads)
     if a.calib_copy:
         line["calib_copy"] = run_calib_copy(torch)
     line["cpu_baseline"] = None if a.no_cpu else run_cpu_baseline(d, workloads)

@@ -52,7 +52,11 @@ namespace bl {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;  // 4
-constexpr int kGemvDepth = 2;                      // row groups in flight per wave
+constexpr int kGemvDepth = 2;                      // row groups in flight per wave (2-bit)
+#ifndef BL_GEMV_SIGN_DEPTH
+#define BL_GEMV_SIGN_DEPTH 4
+#endif
+constexpr int kGemvSignDepth = BL_GEMV_SIGN_DEPTH;  // the 1-bit rows carry half the bytes
 constexpr int kGemvMaxC = 512;                     // K <= 32768
 
 struct GemvProj {
@@ -245,9 +249,10 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   // The weight ring goes out before the activations: vector loads complete in issue
   // order, so this way the first row waits for one memory latency, not two in a row.
   // The two scales come through the scalar cache, off the vector counter.
-  uint4 w[kGemvDepth][I];
+  constexpr int D = FMT == 0 ? kGemvDepth : kGemvSignDepth;
+  uint4 w[D][I];
 #pragma unroll
-  for (int d = 0; d < kGemvDepth; ++d) load_w(w[d]);
+  for (int d = 0; d < D; ++d) load_w(w[d]);
   // activations: 2-bit chunks as 4 transposed uint4, 1-bit chunks as 4 x 8 bit planes
   uint4 x[FMT == 0 ? I : 1][4];
   uint32_t x1[FMT == 1 ? I : 1][4][8];
@@ -328,13 +333,13 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   // (already in flight) straight-line: no exit in the middle of the ring, so the wait
   // before each group is for its own buffer only.
   int left = (glast - g0) / stride + 1;
-  while (left >= kGemvDepth) {
+  while (left >= D) {
 #pragma unroll
-    for (int d = 0; d < kGemvDepth; ++d) step(d, true);
-    left -= kGemvDepth;
+    for (int d = 0; d < D; ++d) step(d, true);
+    left -= D;
   }
 #pragma unroll
-  for (int d = 0; d < kGemvDepth - 1; ++d)
+  for (int d = 0; d < D - 1; ++d)
     if (d < left) step(d, false);
   flush();
 }

@@ -25,6 +25,9 @@ and the 1-bit sign variant (the original BitNet weight binarization):
   S4. eight codes per byte, code k = 8j+i in bit i of byte j, set for +1
   S5. acc = Xq . codes^T in integers, Y = fp32(acc * beta / s_t)
 
+and group quantization: G blocks of N/G output rows, each quantized alone (beta_g);
+Y[t, o] = fp32(acc * beta_{o // (N/G)} / s_t).
+
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (brute force in exact rationals, library routines, closed forms, invariants and the
 worked examples under ``tests/golden/``).
@@ -94,6 +97,8 @@ def _load():
                 "orc_product": [P, P, I64, I64, I64, P],
                 "orc_rescale": [P, P, ctypes.c_float, I64, I64, P],
                 "orc_forward": [P, P, I64, I64, P, ctypes.c_float, I64, P, P],
+                "orc_quantize_weights_groups": [P, I64, I64, I64, P, P, P],
+                "orc_rescale_groups": [P, P, P, I64, I64, I64, P],
                 "orc_sum": [P, I64, P],
                 "orc_sign_codes": [P, I64, ctypes.c_double, P],
                 "orc_sign_weights": [P, I64, I64, P, P, P, P],
@@ -339,3 +344,35 @@ def bitlinear_sign(X, W, gain=None, eps=1e-6, flags=0):
     Y, acc = forward_sign(Xq, s, P, beta)
     return {"packed": P, "codes": c, "alpha": alpha, "beta": beta, "gamma": gamma, "Xq": Xq,
             "x_scale": s, "acc": acc, "Y": Y}
+
+
+# ---------------------------------------------------------------- group quantization
+
+def quantize_weights_groups(W, G):
+    """W [N, K] fp32, G | N -> (packed [N, K/4], beta fp32 [G], gamma fp64 [G])."""
+    W = _f32(W)
+    N, K = W.shape
+    P = np.empty((N, K // 4), dtype=np.uint8)
+    b = np.empty(G, dtype=np.float32)
+    g = np.empty(G, dtype=np.float64)
+    _check(_load().orc_quantize_weights_groups(_ptr(W), N, K, int(G), _ptr(P), _ptr(b), _ptr(g)))
+    return P, b, g
+
+
+def rescale_groups(acc, s, beta):
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s = _f32(s)
+    beta = _f32(beta)
+    T, N = acc.shape
+    Y = np.empty((T, N), dtype=np.float32)
+    _check(_load().orc_rescale_groups(_ptr(acc), _ptr(s), _ptr(beta), T, N, beta.size, _ptr(Y)))
+    return Y
+
+
+def bitlinear_groups(X, W, G, gain=None, eps=1e-6, flags=0):
+    """The forward with G weight scale groups; returns a dict of stages."""
+    P, beta, gamma = quantize_weights_groups(W, G)
+    Xq, s = quantize_acts(X, gain, eps, flags)
+    acc = product(Xq, P, W.shape[1])
+    return {"packed": P, "beta": beta, "gamma": gamma, "Xq": Xq, "x_scale": s, "acc": acc,
+            "Y": rescale_groups(acc, s, beta)}

@@ -59,6 +59,13 @@
  *       is the scale that minimizes the L2 error of a sign code).
  *   S4. eight codes per byte: code k = 8j+i in bit i of byte j, 1 for +1, 0 for -1.
  *   S5. acc = sum_k Xq[t,k] * c[o,k] in integers; Y = fp32(acc * beta / s_t) in fp64.
+ *
+ * Group quantization ([bitnet.cpp] "Group quantization and normalization": weights and
+ * activations split into G groups whose parameters are estimated separately, so that
+ * no group needs another's): the weight matrix is cut into G blocks of N/G consecutive
+ * output rows, and steps 1-2 run on each block alone (beta_g); activations are already
+ * scaled per token (step 5), and RMSNorm is per token. The rescale of row o uses the
+ * scale of its block: Y[t,o] = fp32(acc * beta_{o / (N/G)} / s_t) in fp64.
  */
 #include <float.h>
 #include <math.h>
@@ -517,4 +524,32 @@ int orc_forward_sign(const int8_t* Xq, const float* s, int64_t T, int64_t K, con
   if (!st) st = orc_rescale(a, s, beta, T, N, Y);
   if (!acc) free(a);
   return st;
+}
+
+/* ---------------------------------------------------------------- group quantization */
+
+/* Steps 1-3 on each of G blocks of N/G rows: P [N, K/4], beta [G], gamma [G]. */
+int orc_quantize_weights_groups(const float* W, int64_t N, int64_t K, int64_t G, uint8_t* P,
+                                float* beta, double* gamma) {
+  if (N <= 0 || K <= 0 || K % 4 || G <= 0 || N % G) return ORC_DIM;
+  const int64_t rows = N / G;
+  for (int64_t g = 0; g < G; ++g) {
+    int st = orc_quantize_weights(W + g * rows * K, rows, K, P + g * rows * (K / 4), &beta[g],
+                                  &gamma[g]);
+    if (st) return st;
+  }
+  return ORC_OK;
+}
+
+/* Y [T, N] = acc * beta_{o / (N/G)} / s_t in fp64, rounded once to fp32. */
+int orc_rescale_groups(const int32_t* acc, const float* s, const float* beta, int64_t T,
+                       int64_t N, int64_t G, float* Y) {
+  if (T <= 0 || N <= 0 || G <= 0 || N % G) return ORC_DIM;
+  const int64_t rows = N / G;
+  for (int64_t t = 0; t < T; ++t) {
+    const double st = (double)s[t];
+    for (int64_t o = 0; o < N; ++o)
+      Y[t * N + o] = (float)((double)acc[t * N + o] * (double)beta[o / rows] / st);
+  }
+  return ORC_OK;
 }

@@ -503,3 +503,54 @@ def test_sign_forward_equals_dequantized_matmul():
     deq = (out["Xq"].astype(np.float64) / out["x_scale"].astype(np.float64)[:, None]) @ \
           (out["codes"].astype(np.float64) * float(out["beta"])).T
     assert np.allclose(out["Y"].astype(np.float64), deq, rtol=1e-6, atol=1e-6 * np.abs(deq).max())
+
+
+# ---------------------------------------------------------------- group quantization
+
+def test_golden_weight_groups():
+    g = load("weight_groups.txt")
+    W = np.array(g["W"], np.float32)
+    P, beta, gamma = oracle.quantize_weights_groups(W, g["G"])
+    assert beta.tolist() == g["beta"] and P.tolist() == g["packed"]
+    acc = oracle.product(np.array(g["Xq"], np.int8), P, W.shape[1])
+    assert acc.tolist() == g["acc"]
+    s = np.array(g["s"], np.float32)
+    assert oracle.rescale_groups(acc, s, beta).tolist() == g["Y"]
+    P1, b1, _ = oracle.quantize_weights(W)
+    assert oracle.rescale(oracle.product(np.array(g["Xq"], np.int8), P1, 4), s, b1).tolist() == \
+        g["Y_one_scale"]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_weight_groups_are_independent_blocks(G):
+    # each block's scale and codes are those of the block quantized alone; G = 1 is the
+    # per-tensor quantizer; scaling one block by 2^k changes only that block's scale
+    r = np.random.default_rng(G)
+    W = (r.standard_normal((64, 256)) * np.repeat(r.uniform(0.005, 0.05, G), 64 // G)[:, None]
+         ).astype(np.float32)
+    P, beta, gamma = oracle.quantize_weights_groups(W, G)
+    rows = 64 // G
+    for g in range(G):
+        Pg, bg, gg = oracle.quantize_weights(W[g * rows:(g + 1) * rows])
+        assert beta[g] == bg and gamma[g] == gg
+        assert np.array_equal(P[g * rows:(g + 1) * rows], Pg)
+    if G == 1:
+        P1, b1, g1 = oracle.quantize_weights(W)
+        assert np.array_equal(P, P1) and beta[0] == b1
+    W2 = W.copy()
+    W2[:rows] *= np.float32(8.0)
+    P2, beta2, _ = oracle.quantize_weights_groups(W2, G)
+    assert beta2[0] == beta[0] * np.float32(8.0) and np.array_equal(P2, P)
+    assert np.array_equal(beta2[1:], beta[1:])
+
+
+def test_weight_groups_rescale_exact():
+    r = np.random.default_rng(3)
+    acc = r.integers(-2 ** 20, 2 ** 20, (3, 12)).astype(np.int32)
+    s = r.uniform(1.0, 300.0, 3).astype(np.float32)
+    beta = r.uniform(0.005, 0.05, 4).astype(np.float32)
+    Y = oracle.rescale_groups(acc, s, beta)
+    for t in range(3):
+        for o in range(12):
+            exact = Fraction(int(acc[t, o])) * Fraction(float(beta[o // 3])) / Fraction(float(s[t]))
+            assert Y[t, o] == np.float32(float(exact))

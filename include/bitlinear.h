@@ -188,6 +188,32 @@ typedef struct bl_proj_desc {
 bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_t T,
                                     bl_stream_t stream);
 
+/* ---------------------------------------------------------------- weight scale groups
+ *
+ * Group quantization ([bitnet.cpp] "Group quantization and normalization": weights and
+ * activations are split into G groups whose parameters are estimated separately, so
+ * that no group needs another's). The weights are cut into G blocks of N/G consecutive
+ * output rows (a tensor-parallel shard each); every block is quantized exactly as
+ * bitlinear_quantize_weights quantizes a whole matrix, with its own beta_g. Activation
+ * scales are per token already (bitlinear_quantize_acts). The forward is that of
+ * bitlinear_forward with row o rescaled by the scale of its block:
+ *   Y[t, o] = fp32(acc) * fp32(beta_{o / (N/G)} / s_t)
+ * Arguments as for bitlinear_quantize_weights / bitlinear_forward_ex, plus:
+ *   G        1 <= G, N % G == 0 (G = 1 is the per-tensor quantizer); else BL_ERR_ARG
+ *   w_scale  device fp32 [G] (beta per block); w_gamma fp64 [G] or NULL
+ * The quantizer runs the per-tensor kernels once per block on the stream. */
+bl_status bitlinear_quantize_weights_scale_groups(const float* W, int64_t N, int64_t K, int64_t G,
+                                                  uint8_t* W_packed, float* w_scale,
+                                                  double* w_gamma, void* workspace,
+                                                  size_t workspace_bytes, bl_stream_t stream);
+bl_status bitlinear_forward_scale_groups(const int8_t* Xq, const float* x_scale, int64_t T,
+                                         int64_t K, const uint8_t* W_packed, const float* w_scale,
+                                         int64_t N, int64_t G, float* Y, int32_t* acc,
+                                         bl_kernel kernel, bl_stream_t stream);
+/* bitlinear_forward_grouped where entry i has groups[i] weight scale groups. */
+bl_status bitlinear_forward_grouped_scale_groups(const bl_proj_desc* descs, const int64_t* groups,
+                                                 int count, int64_t T, bl_stream_t stream);
+
 /* ---------------------------------------------------------------- 1-bit sign variant
  *
  * The original BitNet weight binarization ([bitnet.cpp] "1. Weight binarization":

@@ -79,6 +79,12 @@ _c_qws = _sig("bitlinear_quantize_weights_sign",
 _c_fws = _sig("bitlinear_forward_sign", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P])
 _c_fwsg = _sig("bitlinear_forward_sign_grouped",
                [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
+_c_qwsg = _sig("bitlinear_quantize_weights_scale_groups",
+               [_P, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P])
+_c_fwsg_scale = _sig("bitlinear_forward_scale_groups",
+                     [_P, _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, ctypes.c_int, _P])
+_c_fwg_scale = _sig("bitlinear_forward_grouped_scale_groups",
+                    [ctypes.POINTER(_ProjDesc), ctypes.POINTER(_I64), ctypes.c_int, _I64, _P])
 _c_str = _sig("bitlinear_status_str", [ctypes.c_int], ctypes.c_char_p)
 _c_err = _sig("bitlinear_last_hip_error", [], ctypes.c_char_p)
 _c_ver = _sig("bitlinear_abi_version", [])
@@ -209,6 +215,48 @@ def bitlinear_forward_sign_grouped(entries, T, stream=None):
            "bitlinear_forward_sign_grouped")
 
 
+def bitlinear_quantize_weights_scale_groups(W, G, W_packed, w_scale, w_gamma, workspace,
+                                            stream=None):
+    N, K = W.shape
+    _check(_c_qwsg(_ptr(W), N, K, int(G), _ptr(W_packed), _ptr(w_scale), _ptr(w_gamma),
+                   _ptr(workspace),
+                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                   _stream(W, stream)), "bitlinear_quantize_weights_scale_groups")
+
+
+def bitlinear_forward_scale_groups(Xq, x_scale, W_packed, w_scale, G, Y, acc=None, kernel="auto",
+                                   stream=None):
+    T, K = Xq.shape
+    N = W_packed.shape[0]
+    k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check(_c_fwsg_scale(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, int(G),
+                         _ptr(Y), _ptr(acc), k, _stream(Xq, stream)),
+           "bitlinear_forward_scale_groups")
+
+
+def bitlinear_forward_grouped_scale_groups(entries, groups, T, stream=None):
+    """entries as for bitlinear_forward_grouped; groups[i] = scale groups of entry i."""
+    g = (_I64 * len(groups))(*[int(x) for x in groups])
+    _check(_c_fwg_scale(_proj_array(entries), g, len(entries), T, _stream(entries[0][0], stream)),
+           "bitlinear_forward_grouped_scale_groups")
+
+
+class _PreparedScaleGroups:
+    def __init__(self, entries, groups, T):
+        self._arr = _proj_array(entries)
+        self._g = (_I64 * len(groups))(*[int(x) for x in groups])
+        self._n, self._T = len(entries), T
+        self._keep = [t for e in entries for t in e if t is not None]
+
+    def __call__(self, stream=None):
+        _check(_c_fwg_scale(self._arr, self._g, self._n, self._T, _stream(self._keep[0], stream)),
+               "bitlinear_forward_grouped_scale_groups")
+
+
+def prepare_forward_grouped_scale_groups(entries, groups, T):
+    return _PreparedScaleGroups(entries, groups, T)
+
+
 class PreparedCall:
     """A grouped ABI call with its descriptor array marshalled once. Calling it
     launches on the current stream at call time (so it can be captured into a graph)."""
@@ -260,6 +308,28 @@ def quantize_weights(W: torch.Tensor, with_gamma: bool = False):
     ws = torch.empty(bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
     bitlinear_quantize_weights(W, packed, beta, gamma, ws)
     return (packed, beta, gamma) if with_gamma else (packed, beta)
+
+
+def quantize_weights_scale_groups(W: torch.Tensor, G: int, with_gamma: bool = False):
+    """W fp32 [N, K], G | N -> (packed uint8 [N, K/4], beta fp32 [G][, gamma fp64 [G]])."""
+    N, K = W.shape
+    dev = W.device
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    beta = torch.empty(G, dtype=torch.float32, device=dev)
+    gamma = torch.empty(G, dtype=torch.float64, device=dev) if with_gamma else None
+    ws = torch.empty(bitlinear_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    bitlinear_quantize_weights_scale_groups(W, G, packed, beta, gamma, ws)
+    return (packed, beta, gamma) if with_gamma else (packed, beta)
+
+
+def forward_scale_groups(Xq, x_scale, packed, beta, with_acc: bool = False, kernel="auto"):
+    """As forward(), with beta fp32 [G] (G | N): row o uses beta[o // (N / G)]."""
+    T = Xq.shape[0]
+    N = packed.shape[0]
+    Y = torch.empty((T, N), dtype=torch.float32, device=Xq.device)
+    acc = torch.empty((T, N), dtype=torch.int32, device=Xq.device) if with_acc else None
+    bitlinear_forward_scale_groups(Xq, x_scale, packed, beta, beta.numel(), Y, acc, kernel)
+    return (Y, acc) if with_acc else Y
 
 
 def quantize_weights_sign(W: torch.Tensor):

@@ -69,7 +69,7 @@ bool supports(bl_kernel k, int64_t T, int64_t N, int64_t K) {
 
 bl_proj_internal to_internal(const int8_t* Xq, const float* xs, int64_t K, const uint8_t* W,
                              const float* ws, int64_t N, float* Y, int32_t* acc) {
-  return bl_proj_internal{Xq, xs, W, ws, Y, acc, (int)N, (int)K};
+  return bl_proj_internal{Xq, xs, W, ws, Y, acc, (int)N, (int)K, (int)N};
 }
 
 hipError_t run(bl_kernel k, const bl_proj_internal* p, int count, int T, hipStream_t s) {
@@ -182,6 +182,73 @@ bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_
     if (s != BL_OK) return s;
   }
   return BL_OK;
+}
+
+bl_status bitlinear_quantize_weights_scale_groups(const float* W, int64_t N, int64_t K, int64_t G,
+                                                  uint8_t* W_packed, float* w_scale,
+                                                  double* w_gamma, void* workspace,
+                                                  size_t workspace_bytes, bl_stream_t stream) {
+  if (!W || !W_packed || !w_scale) return BL_ERR_NULL;
+  if (N <= 0 || K <= 0 || K % 4 || N > kMaxRows || N * K > kMaxWeights) return BL_ERR_DIM;
+  if (G < 1 || N % G) return BL_ERR_ARG;
+  if (!workspace || workspace_bytes < bitlinear_weight_workspace_bytes(N, K))
+    return BL_ERR_WORKSPACE;
+  if (!aligned16(W) || !aligned16(workspace) || !aligned_n(w_scale, 4) ||
+      (w_gamma && !aligned_n(w_gamma, 8)))
+    return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  const int64_t rows = N / G;
+  // one block of rows after the other on the stream (the workspace is reused)
+  for (int64_t g = 0; g < G; ++g) {
+    bl_status s = hip_status(bl_launch_quantize_weights(
+        W + g * rows * K, rows, K, W_packed + g * rows * (K / 4), w_scale + g,
+        w_gamma ? w_gamma + g : nullptr, workspace, (hipStream_t)stream));
+    if (s != BL_OK) return s;
+  }
+  return BL_OK;
+}
+
+bl_status bitlinear_forward_grouped_scale_groups(const bl_proj_desc* descs, const int64_t* groups,
+                                                 int count, int64_t T, bl_stream_t stream) {
+  if (!descs || !groups) return BL_ERR_NULL;
+  if (count < 1 || count > BL_MAX_GROUP) return BL_ERR_ARG;
+  bl_proj_internal p[BL_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    const bl_proj_desc& d = descs[i];
+    bl_status s = check_proj(d.Xq, d.x_scale, T, d.K, d.W_packed, d.w_scale, d.N, d.Y, d.acc);
+    if (s != BL_OK) return s;
+    if (groups[i] < 1 || d.N % groups[i]) return BL_ERR_ARG;
+    p[i] = to_internal(d.Xq, d.x_scale, d.K, d.W_packed, d.w_scale, d.N, d.Y, d.acc);
+    p[i].rpg = (int)(d.N / groups[i]);
+  }
+  (void)hipGetLastError();
+  bl_proj_internal batch[BL_MAX_GROUP];
+  const bl_kernel kinds[4] = {BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_PREFILL,
+                              BL_KERNEL_GENERIC};
+  for (bl_kernel k : kinds) {
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+      if (choose(T, descs[i].N, descs[i].K) == k) batch[n++] = p[i];
+    if (n == 0) continue;
+    bl_status s = hip_status(run(k, batch, n, (int)T, (hipStream_t)stream));
+    if (s != BL_OK) return s;
+  }
+  return BL_OK;
+}
+
+bl_status bitlinear_forward_scale_groups(const int8_t* Xq, const float* x_scale, int64_t T,
+                                         int64_t K, const uint8_t* W_packed, const float* w_scale,
+                                         int64_t N, int64_t G, float* Y, int32_t* acc,
+                                         bl_kernel kernel, bl_stream_t stream) {
+  bl_status s = check_proj(Xq, x_scale, T, K, W_packed, w_scale, N, Y, acc);
+  if (s != BL_OK) return s;
+  if (G < 1 || N % G) return BL_ERR_ARG;
+  if (kernel == BL_KERNEL_AUTO) kernel = choose(T, N, K);
+  if (!supports(kernel, T, N, K)) return BL_ERR_ARG;
+  bl_proj_internal p = to_internal(Xq, x_scale, K, W_packed, w_scale, N, Y, acc);
+  p.rpg = (int)(N / G);
+  (void)hipGetLastError();
+  return hip_status(run(kernel, &p, 1, (int)T, (hipStream_t)stream));
 }
 
 bl_status bitlinear_quantize_weights_sign(const float* W, int64_t N, int64_t K, uint8_t* W_bits,

@@ -70,6 +70,7 @@ struct GemvProj {
   int wg0, nwg;  // this projection's workgroups
   int cfg;       // mapping (see gemv_kernel)
   int CW;        // chunks per wave segment
+  int rpg;       // rows per weight scale group
 };
 
 struct GemvArgs {
@@ -96,6 +97,7 @@ __device__ __forceinline__ GemvProj load_proj(ArgsPtr a, int i) {
   P.nwg = a->p[i].nwg;
   P.cfg = a->p[i].cfg;
   P.CW = a->p[i].CW;
+  P.rpg = a->p[i].rpg;
   return P;
 }
 
@@ -263,7 +265,9 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
     else load_act_chunk1(P.Xq, ci[i], on[i], x1[i], xsum);
   }
   typedef const float __attribute__((address_space(4)))* ConstF;
-  const float f = *(ConstF)P.ws / *(ConstF)P.xs;
+  const float xsc = *(ConstF)P.xs;
+  const float f = *(ConstF)P.ws / xsc;  // one weight scale (rpg >= N)
+  const bool scale_groups = P.rpg < P.N;
   int g = g0, k = 0;
   // Row totals wait in a register (lane j holds slot j) and leave in one store per 64
   // slots: no store sits between the ring's loads, so each wait counts loads only.
@@ -273,7 +277,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   auto flush = [&]() {
     const int row = (gb + (lane / RW) * stride) * RW + lane % RW;
     if (lane < nb && ((keep >> lane) & 1ull) && row < P.N) {
-      P.Y[row] = (float)res * f;
+      P.Y[row] = (float)res * (scale_groups ? P.ws[row / P.rpg] / xsc : f);
       if (P.acc) P.acc[row] = res;
     }
     nb = 0;
@@ -471,6 +475,7 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     g.C = (int)(p[i].K / kCodes);
     g.cfg = c.cfg;
     g.CW = (g.C + c.S - 1) / c.S;
+    g.rpg = p[i].rpg;
     const int groups = (g.N + c.RW - 1) / c.RW;
     const int gpw = kGemvWaves / c.S;
     int64_t n = (cost[i] * (int64_t)(cap - count) + total - 1) / total;

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void generic_kernel(bl_proj_internal p, int T)
       acc += (int)x[4 * j + i] * q;
     }
   }
-  const float f = p.w_scale[0] / p.x_scale[t];
+  const float f = p.w_scale[o / p.rpg] / p.x_scale[t];
   p.Y[(int64_t)t * p.N + o] = (float)acc * f;
   if (p.acc) p.acc[(int64_t)t * p.N + o] = acc;
 }

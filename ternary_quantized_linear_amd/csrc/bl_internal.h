@@ -18,6 +18,7 @@ struct bl_proj_internal {
   int32_t* acc;
   int N;
   int K;
+  int rpg;  // rows per weight scale group: row o uses w_scale[o / rpg] (rpg = N: one scale)
 };
 
 size_t bl_weight_workspace_bytes_impl(int64_t N, int64_t K);

@@ -53,6 +53,7 @@ struct PfArgs {
   int T, N, K;
   int tiles_m, tiles_n;
   int per_xcd;  // logical tiles per XCD
+  int rpg;      // rows per weight scale group
 };
 
 template <int BM, int BN>
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int Kb = a.K >> 2;
   const int nk = a.K / kPfKT;
-  const float beta = a.ws[0];
+  const float beta = a.ws[n0 / a.rpg];
   for (int i = tid; i < BM; i += kPfThreads) {
     const int t = m0 + i;
     fac[i] = t < a.T ? beta / a.xs[t] : 0.0f;
@@ -187,7 +188,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
         const int t = m0 + tb + dt;
         if (t < a.T && n < a.N) {
           const int v = acc[i][j][r];
-          yp[(int64_t)dt * a.N] = (float)v * fac[tb + dt];
+          // fac holds beta of the tile's first row's group; rows of another group (scale
+          // groups smaller than the tile or straddling it) divide their own scale
+          const float f = n / a.rpg == n0 / a.rpg ? fac[tb + dt] : a.ws[n / a.rpg] / a.xs[t];
+          yp[(int64_t)dt * a.N] = (float)v * f;
           if (ap) ap[(int64_t)dt * a.N] = v;
         }
       }
@@ -207,6 +211,7 @@ hipError_t launch_prefill_t(const bl_proj_internal* p, int T, hipStream_t stream
   a.T = T;
   a.N = p->N;
   a.K = p->K;
+  a.rpg = p->rpg;
   a.tiles_m = (T + BM - 1) / BM;
   a.tiles_n = (p->N + BN - 1) / BN;
   const int tiles = a.tiles_m * a.tiles_n;

@@ -62,6 +62,7 @@ struct SkProj {
   int S, teams;  // waves per team, teams per workgroup
   int npass;     // passes of a team over the segments
   int R;         // row blocks per team
+  int rpg;       // rows per weight scale group
   int wg0, nwg;
 };
 
@@ -91,6 +92,7 @@ __device__ __forceinline__ SkProj load_sk(SkArgsPtr a, int i) {
   P.teams = a->p[i].teams;
   P.npass = a->p[i].npass;
   P.R = a->p[i].R;
+  P.rpg = a->p[i].rpg;
   P.wg0 = a->p[i].wg0;
   P.nwg = a->p[i].nwg;
   return P;
@@ -252,12 +254,17 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
         for (int r = 0; r < 4; ++r)
           v[r] = __hip_atomic_load(tile + tb * 256 + sk_pos(li, 4 * lg + r), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-        const float f = facs[t];
+        float f = facs[t];
         const bool tin = t < T;
+        float fr[4] = {f, f, f, f};
+        if (P.rpg < P.N) {  // weight scale groups: the scale of each row's group
+#pragma unroll
+          for (int r = 0; r < 4; ++r) fr[r] = P.ws[min(row + r, P.N - 1) / P.rpg] / P.xs[min(t, T - 1)];
+        }
         if (vec_store) {
           const uint32_t off = tin && row < P.N ? ((uint32_t)t * (uint32_t)P.N + (uint32_t)row) * 4u : kOob;
-          const v4i y = v4i{__float_as_int((float)v[0] * f), __float_as_int((float)v[1] * f),
-                            __float_as_int((float)v[2] * f), __float_as_int((float)v[3] * f)};
+          const v4i y = v4i{__float_as_int((float)v[0] * fr[0]), __float_as_int((float)v[1] * fr[1]),
+                            __float_as_int((float)v[2] * fr[2]), __float_as_int((float)v[3] * fr[3])};
           __builtin_amdgcn_raw_buffer_store_b128(y, yr, off, 0, 0);
           if (P.acc) __builtin_amdgcn_raw_buffer_store_b128(v4i{v[0], v[1], v[2], v[3]}, ar, off, 0, 0);
         } else {
@@ -265,7 +272,7 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
           for (int r = 0; r < 4; ++r) {
             const uint32_t off =
                 tin && row + r < P.N ? ((uint32_t)t * (uint32_t)P.N + (uint32_t)(row + r)) * 4u : kOob;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int((float)v[r] * f), yr, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int((float)v[r] * fr[r]), yr, off, 0, 0);
             if (P.acc) __builtin_amdgcn_raw_buffer_store_b32(v[r], ar, off, 0, 0);
           }
         }
@@ -388,6 +395,7 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
     s.N = p[i].N;
     s.K = p[i].K;
     s.nrb = (p[i].N + 15) / 16;
+    s.rpg = p[i].rpg;
     sk_plan(p[i].K, TB, s);
     total += (int64_t)p[i].N * (p[i].K / 4);
   }

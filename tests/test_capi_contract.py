@@ -52,7 +52,9 @@ def test_header_declares_the_abi():
               "bitlinear_quantize_acts_grouped", "bitlinear_weight_workspace_bytes",
               "bitlinear_status_str", "bitlinear_last_hip_error", "bitlinear_abi_version",
               "bitlinear_forward_choice", "bitlinear_quantize_weights_sign",
-              "bitlinear_forward_sign", "bitlinear_forward_sign_grouped"]:
+              "bitlinear_forward_sign", "bitlinear_forward_sign_grouped",
+              "bitlinear_quantize_weights_scale_groups", "bitlinear_forward_scale_groups",
+              "bitlinear_forward_grouped_scale_groups"]:
         assert n in names
 
 
@@ -245,3 +247,31 @@ def test_sign_variant_validation(lib):
     assert fg(pa, 9, 1, None) == BL_ERR_ARG
     pa[1].K = 1028
     assert fg(pa, 2, 1, None) == BL_ERR_DIM
+
+
+def test_scale_groups_validation(lib):
+    f = lib.bitlinear_quantize_weights_scale_groups
+    f.argtypes = [P, I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+    f.restype = ctypes.c_int
+    lib.bitlinear_weight_workspace_bytes.argtypes = [I64, I64]
+    lib.bitlinear_weight_workspace_bytes.restype = ctypes.c_size_t
+    ws = lib.bitlinear_weight_workspace_bytes(256, 1024)
+    assert f(A, 256, 1024, 0, B, C, None, D, ws, None) == BL_ERR_ARG
+    assert f(A, 256, 1024, 3, B, C, None, D, ws, None) == BL_ERR_ARG   # 3 does not divide 256
+    assert f(A, 256, 1024, 8, None, C, None, D, ws, None) == BL_ERR_NULL
+    assert f(A, 256, 1024, 8, B, C, None, D, ws - 1, None) == BL_ERR_WORKSPACE
+    g = lib.bitlinear_forward_scale_groups
+    g.argtypes = [P, P, I64, I64, P, P, I64, I64, P, P, ctypes.c_int, P]
+    g.restype = ctypes.c_int
+    assert g(A, B, 1, 4096, C, D, 4096, 0, E, None, 0, None) == BL_ERR_ARG
+    assert g(A, B, 1, 4096, C, D, 4096, 3, E, None, 0, None) == BL_ERR_ARG
+    assert g(A, B, 2, 4096, C, D, 4096, 8, E, None, 1, None) == BL_ERR_ARG  # gemv: T == 1
+    assert g(None, B, 1, 4096, C, D, 4096, 8, E, None, 0, None) == BL_ERR_NULL
+    fg = lib.bitlinear_forward_grouped_scale_groups
+    fg.argtypes = [ctypes.POINTER(ProjDesc), ctypes.POINTER(I64), ctypes.c_int, I64, P]
+    fg.restype = ctypes.c_int
+    pa = (ProjDesc * 2)(*[ProjDesc(A.value, B.value, C.value, D.value, E.value, None, 64, 1024)
+                          for _ in range(2)])
+    gr = (I64 * 2)(4, 3)
+    assert fg(pa, None, 2, 1, None) == BL_ERR_NULL
+    assert fg(pa, gr, 2, 1, None) == BL_ERR_ARG  # 3 does not divide 64

@@ -401,6 +401,51 @@ def run_sign_decode(torch, bl, workloads, T=1):
             "quantize_weights_gbs_algorithmic": round(wq_bytes / (ms_wq * 1e-3) / 1e9, 1)}
 
 
+def run_scale_groups_decode(torch, bl, workloads, G=8, T=1):
+    """Group quantization on the decode8b layer: every projection's weights in G blocks of
+    output rows with their own scale (a tensor-parallel shard each), grouped GEMV."""
+    dev = torch.device("cuda:0")
+    Ws = workloads.decode8b_layer(0)
+    base = {n: bl.quantize_weights_scale_groups(torch.from_numpy(W).to(dev), G)
+            for n, W in Ws.items()}
+    reps = [base] + [{n: (p.clone(), b.clone()) for n, (p, b) in base.items()}
+                     for _ in range(REPLICAS - 1)]
+    inputs = workloads.decode8b_inputs(T, 100)
+    acts = {}
+    for name, X in inputs.items():
+        acts[name] = bl.quantize_acts(torch.from_numpy(X).to(dev))
+    outs = {p: torch.empty((T, N), dtype=torch.float32, device=dev)
+            for p, (N, K) in workloads.LLAMA3_8B.items()}
+    def timed(groups):
+        fws = []
+        for r in reps:
+            entries = []
+            for name, projs in workloads.LLAMA3_8B_INPUTS.items():
+                Xq, xs = acts[name]
+                for p in projs:
+                    pk, b = r[p]
+                    entries.append((Xq, xs, pk, b, outs[p], None))
+            fws.append(bl.prepare_forward_grouped_scale_groups(entries, [groups] * len(entries), T))
+        n_k = 256
+        g_k = _warm_then_capture(torch, [fws[i % len(fws)] for i in range(n_k)])
+        g_k.replay()
+        return _time_graph(torch, g_k, 2) / n_k
+
+    # the same buffers read with one scale (G = 1: the first block's scale for all rows)
+    # and with the G block scales: the difference is the cost of the grouping alone
+    ms1 = timed(1)
+    ms = timed(G)
+    gemv_b = sum(gemv_bytes(T, N, K) + 4 * (G - 1) for (N, K) in workloads.LLAMA3_8B.values())
+    del reps, base
+    torch.cuda.empty_cache()
+    return {"workload": "decode8b layer, weights in %d scale groups of output rows" % G,
+            "kernel": "gemv_kernel<1, 0> (grouped, 7 projections)", "G": G,
+            "gemv_us": round(ms * 1e3, 3), "gemv_us_same_buffers_one_scale": round(ms1 * 1e3, 3),
+            "gemv_bytes": gemv_b,
+            "gemv_gbs": round(gemv_b / (ms * 1e-3) / 1e9, 1),
+            "gemv_frac_hbm": round(gemv_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def run_calib_copy(torch):
     n = 64 * 1024 * 1024  # 256 MiB of fp32
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -518,6 +563,7 @@ def main():
         line["fullpass"] = run_fullpass(torch, bl, workloads)
         line["weight_quant"] = run_weight_quant(torch, bl, workloads)
         line["sign_decode8b"] = run_sign_decode(torch, bl, workloads)
+        line["scale_groups_decode8b"] = run_scale_groups_decode(torch, bl, workloads)
     if a.calib_copy:
         line["calib_copy"] = run_calib_copy(torch)
     line["cpu_baseline"] = None if a.no_cpu else run_cpu_baseline(d, workloads)

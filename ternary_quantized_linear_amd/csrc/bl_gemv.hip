@@ -268,6 +268,14 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   const float xsc = *(ConstF)P.xs;
   const float f = *(ConstF)P.ws / xsc;  // one weight scale (rpg >= N)
   const bool scale_groups = P.rpg < P.N;
+  // with weight scale groups, each lane's scale for the rows of the first flush is
+  // loaded now, while the weights stream (a load at the flush would add a round trip);
+  // it is first used, and so first waited for, at the flush
+  auto lane_scale = [&](int gbase) {
+    const int row = min((gbase + (lane / RW) * stride) * RW + lane % RW, P.N - 1);
+    return P.ws[row / P.rpg];
+  };
+  const float ws0 = scale_groups ? lane_scale(g0) : 0.0f;
   int g = g0, k = 0;
   // Row totals wait in a register (lane j holds slot j) and leave in one store per 64
   // slots: no store sits between the ring's loads, so each wait counts loads only.
@@ -277,7 +285,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   auto flush = [&]() {
     const int row = (gb + (lane / RW) * stride) * RW + lane % RW;
     if (lane < nb && ((keep >> lane) & 1ull) && row < P.N) {
-      P.Y[row] = (float)res * (scale_groups ? P.ws[row / P.rpg] / xsc : f);
+      P.Y[row] = (float)res * (!scale_groups ? f : (gb == g0 ? ws0 : lane_scale(gb)) / xsc);
       if (P.acc) P.acc[row] = res;
     }
     nb = 0;

@@ -28,6 +28,16 @@ and the 1-bit sign variant (the original BitNet weight binarization):
 and group quantization: G blocks of N/G output rows, each quantized alone (beta_g);
 Y[t, o] = fp32(acc * beta_{o // (N/G)} / s_t).
 
+and the training side (fake quantization with the warm-up lambda and the straight-
+through estimator), in numpy with the roundings written out:
+
+  T1. lambda = min(step / total, 1)
+  T2. W_lam = bf16(W + lam * (beta * q - W)), every operation one fp32 rounding
+  T3. x_lam = bf16(y + lam * (Xq / s - y)) with y the RMSNorm output, Xq / s one fp32
+      division; r = 1/rms per token kept for the backward
+  T4. STE: the gradient of the quantizer output is passed to its input unchanged; the
+      RMSNorm backward in fp64: dx = r g dy - x r^3 (sum g dy x) / K, dg = sum_t r dy x
+
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (brute force in exact rationals, library routines, closed forms, invariants and the
 worked examples under ``tests/golden/``).
@@ -376,3 +386,89 @@ def bitlinear_groups(X, W, G, gain=None, eps=1e-6, flags=0):
     acc = product(Xq, P, W.shape[1])
     return {"packed": P, "beta": beta, "gamma": gamma, "Xq": Xq, "x_scale": s, "acc": acc,
             "Y": rescale_groups(acc, s, beta)}
+
+
+# ---------------------------------------------------------------- training side (numpy)
+# [HF-1.58] "Training with the straight-through estimator (STE)": round() has no useful
+# gradient, so its gradient is taken as 1 and gradients flow as through the identity.
+# [HF-1.58] "Dynamic warm-up quantization": lambda = min(step / total_steps, 1) scales
+# the difference between the quantized and the original values (0: full precision,
+# 1: fully quantized). [HF-1.58] "How quantization works": the quantized weights and
+# activations are rescaled back (dequantized) after rounding.
+
+def warmup_lambda(step, total):
+    """T1: min(step / total, 1), in fp64."""
+    if total <= 0:
+        raise OracleError("bad dimensions")
+    return min(float(step) / float(total), 1.0)
+
+
+def bf16_bits(x):
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even (the top 16
+    bits of the fp32 pattern, plus one unit where the dropped 16 bits exceed half, or
+    equal half with an odd kept part). NaN stays NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    keep = u >> np.uint64(16)
+    low = u & np.uint64(0xFFFF)
+    up = (low > 0x8000) | ((low == 0x8000) & ((keep & np.uint64(1)) == 1))
+    out = (keep + up.astype(np.uint64)).astype(np.uint32)
+    nan = np.isnan(x)
+    out[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint32)
+    return out.astype(np.uint16)
+
+
+def bf16_to_f32(b):
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def fake_quant_weights(W, lam):
+    """T2: W [N, K] fp32, lam -> bf16 bits [N, K] of W + lam * (beta * q - W)."""
+    W = _f32(W)
+    N, K = W.shape
+    _, beta, _ = quantize_weights(W)
+    q = ternarize(W, beta)
+    wq = (q.astype(np.float32) * np.float32(beta)).astype(np.float32)  # exact: q in {-1,0,1}
+    d = (wq - W).astype(np.float32)
+    m = (W + (np.float32(lam) * d).astype(np.float32)).astype(np.float32)
+    return bf16_bits(m)
+
+
+def rms_inv(X, eps=1e-6, flags=0):
+    """1 / sqrt(exact sum x^2 / K + eps) per token in fp64 (1 with NO_NORM)."""
+    X = _f32(X)
+    T, K = X.shape
+    if flags & NO_NORM:
+        return np.ones(T, np.float64)
+    return np.array([1.0 / np.sqrt(sum_sq(X[t]) / K + float(np.float32(eps))) for t in range(T)])
+
+
+def fake_quant_acts(X, gain=None, eps=1e-6, flags=0, lam=1.0):
+    """T3: -> (bf16 bits [T, K] of y + lam * (Xq / s - y), Xq, s, r)."""
+    X = _f32(X)
+    y = X.copy() if flags & NO_NORM else rmsnorm(X, gain, eps)
+    Xq, s = absmax_quant(y)
+    xd = (Xq.astype(np.float32) / s[:, None]).astype(np.float32)  # one fp32 division
+    d = (xd - y).astype(np.float32)
+    m = (y + (np.float32(lam) * d).astype(np.float32)).astype(np.float32)
+    return bf16_bits(m), Xq, s, rms_inv(X, eps, flags)
+
+
+def rmsnorm_backward(X, gain, r, dY):
+    """T4 (the norm part; the quantizers pass gradients through): dX [T, K] fp32 and
+    dgain [K] fp32 (None without gain), all arithmetic in fp64, one rounding each."""
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    r = np.asarray(r, np.float64)
+    T, K = X.shape
+    g = np.ones(K) if gain is None else np.asarray(gain, np.float64)
+    gdy = dY * g[None, :]
+    c = np.array([math_fsum(gdy[t] * X[t]) for t in range(T)])
+    dX = r[:, None] * gdy - X * (r ** 3 * c / K)[:, None]
+    dg = None if gain is None else np.array([math_fsum(dY[:, k] * X[:, k] * r) for k in range(K)])
+    return dX.astype(np.float32), (None if dg is None else dg.astype(np.float32))
+
+
+def math_fsum(v):
+    import math
+    return math.fsum(np.asarray(v, np.float64).tolist())

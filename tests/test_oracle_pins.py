@@ -554,3 +554,112 @@ def test_weight_groups_rescale_exact():
         for o in range(12):
             exact = Fraction(int(acc[t, o])) * Fraction(float(beta[o // 3])) / Fraction(float(s[t]))
             assert Y[t, o] == np.float32(float(exact))
+
+
+# ---------------------------------------------------------------- training side
+
+def test_golden_train_fake_quant():
+    g = load("train_fake_quant.txt")
+    Wl = oracle.fake_quant_weights(np.array(g["W"], np.float32), g["W_lam"])
+    assert oracle.bf16_to_f32(Wl).tolist() == g["W_out"]
+    Xl, Xq, s, r = oracle.fake_quant_acts(np.array(g["X"], np.float32), flags=oracle.NO_NORM,
+                                          lam=g["X_lam"])
+    assert oracle.bf16_to_f32(Xl).tolist() == g["X_out"]
+    assert [oracle.warmup_lambda(t, 1000) for t in g["lam_steps"]] == g["lam_values"]
+
+
+def _bf16_brute(v):
+    # the two bf16 values around v, the nearer by exact comparison, ties to the even one
+    b = np.float32(v).view(np.uint32)
+    lo = (int(b) >> 16) & 0xFFFF
+    cand = [lo, lo + 1]
+    vals = [Fraction(float(np.array([c << 16], np.uint32).view(np.float32)[0])) for c in cand]
+    x = Fraction(float(v))
+    d0, d1 = abs(x - vals[0]), abs(x - vals[1])
+    if d0 < d1 or (d0 == d1 and lo % 2 == 0):
+        return lo
+    return lo + 1
+
+
+def test_bf16_rounding_against_brute_force():
+    r = np.random.default_rng(8)
+    v = (r.standard_normal(3000) * np.exp(r.uniform(-20, 20, 3000))).astype(np.float32)
+    # ties and near-ties: patterns with low half exactly 0x8000 and 0x8000 +- 1
+    u = r.integers(0, 2 ** 31, 300, dtype=np.int64).astype(np.uint32) & np.uint32(0x7F7F0000)
+    ties = np.concatenate([(u | 0x8000), (u | 0x8001), (u | 0x7FFF)]).view(np.float32)
+    v = np.concatenate([v, ties, np.array([0.0, -0.0, 1.0, -1.0], np.float32)])
+    got = oracle.bf16_bits(v)
+    for x, b in zip(v, got):
+        assert int(b) == _bf16_brute(x), x
+    assert oracle.bf16_bits(np.array([np.inf, -np.inf], np.float32)).tolist() == [0x7F80, 0xFF80]
+    assert np.isnan(oracle.bf16_to_f32(oracle.bf16_bits(np.array([np.nan], np.float32))))[0]
+
+
+def test_fake_quant_lambda_limits():
+    # lambda = 0: the original values (bf16-rounded); lambda = 1: the dequantized values,
+    # exactly where the difference is exact (Sterbenz: within a factor 2), else within one
+    # fp32 rounding before the bf16 one
+    r = np.random.default_rng(12)
+    W = (r.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    assert np.array_equal(oracle.fake_quant_weights(W, 0.0), oracle.bf16_bits(W))
+    _, beta, _ = oracle.quantize_weights(W)
+    deq = (oracle.ternarize(W, beta).astype(np.float32) * beta).astype(np.float32)
+    w1 = oracle.bf16_to_f32(oracle.fake_quant_weights(W, 1.0)).astype(np.float64)
+    ref = oracle.bf16_to_f32(oracle.bf16_bits(deq)).astype(np.float64)
+    tol = 2.0 ** -7 * np.maximum(np.abs(W), np.abs(deq)).astype(np.float64)
+    assert np.all(np.abs(w1 - ref) <= tol)
+    sterbenz = (deq != 0) & (np.abs(W) <= 2 * np.abs(deq)) & (np.abs(deq) <= 2 * np.abs(W))
+    assert np.array_equal(w1[sterbenz], ref[sterbenz])
+    X = r.standard_normal((4, 512)).astype(np.float32)
+    xl0, Xq, s, _ = oracle.fake_quant_acts(X, lam=0.0)
+    assert np.array_equal(xl0, oracle.bf16_bits(oracle.rmsnorm(X)))
+
+
+def _rmsnorm64(X, g, eps):
+    X = np.asarray(X, np.float64)
+    r = 1.0 / np.sqrt((X * X).mean(axis=1) + eps)
+    return X * r[:, None] * g[None, :]
+
+
+@pytest.mark.parametrize("with_gain", [False, True])
+def test_rmsnorm_backward_finite_differences(with_gain):
+    # central differences of the fp64 forward: the loss sum(dY * y(X))
+    r = np.random.default_rng(21)
+    T, K, eps = 3, 16, 1e-6
+    X = r.standard_normal((T, K))
+    g = r.uniform(0.5, 1.5, K) if with_gain else np.ones(K)
+    dY = r.standard_normal((T, K))
+    rr = 1.0 / np.sqrt((X * X).mean(axis=1) + eps)
+    dX, dg = oracle.rmsnorm_backward(X, g if with_gain else None, rr, dY)
+    h = 1e-6
+    for t in range(T):
+        for k in range(K):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[t, k] += h
+            Xm[t, k] -= h
+            num = (np.sum(dY * _rmsnorm64(Xp, g, eps)) - np.sum(dY * _rmsnorm64(Xm, g, eps))) / (2 * h)
+            assert abs(num - dX[t, k]) <= 1e-5 * max(1.0, abs(num))
+    if with_gain:
+        for k in range(K):
+            gp, gm = g.copy(), g.copy()
+            gp[k] += h
+            gm[k] -= h
+            num = (np.sum(dY * _rmsnorm64(X, gp, eps)) - np.sum(dY * _rmsnorm64(X, gm, eps))) / (2 * h)
+            assert abs(num - dg[k]) <= 1e-5 * max(1.0, abs(num))
+
+
+def test_rmsnorm_backward_against_autograd():
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(22)
+    T, K, eps = 5, 64, 1e-6
+    X = r.standard_normal((T, K))
+    g = r.uniform(0.5, 1.5, K)
+    dY = r.standard_normal((T, K))
+    xt = torch.tensor(X, dtype=torch.float64, requires_grad=True)
+    gt = torch.tensor(g, dtype=torch.float64, requires_grad=True)
+    y = xt * torch.rsqrt((xt * xt).mean(dim=1, keepdim=True) + eps) * gt
+    y.backward(torch.tensor(dY, dtype=torch.float64))
+    rr = 1.0 / np.sqrt((X * X).mean(axis=1) + eps)
+    dX, dg = oracle.rmsnorm_backward(X, g, rr, dY)
+    assert np.allclose(dX, xt.grad.numpy(), rtol=1e-6, atol=1e-7)
+    assert np.allclose(dg, gt.grad.numpy(), rtol=1e-6, atol=1e-7)

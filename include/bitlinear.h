@@ -248,6 +248,48 @@ bl_status bitlinear_forward_sign(const int8_t* Xq, const float* x_scale, int64_t
 bl_status bitlinear_forward_sign_grouped(const bl_proj_desc* descs, int count, int64_t T,
                                          bl_stream_t stream);
 
+/* ---------------------------------------------------------------- training side
+ *
+ * Fake quantization with the warm-up lambda and the straight-through estimator
+ * ([HF-1.58] "Dynamic warm-up quantization": lambda = min(step / total_steps, 1) scales
+ * the difference between quantized and original values, x + lambda (Q(x) - x);
+ * "Training with the straight-through estimator (STE)": the gradient of round() is
+ * taken as 1, so a quantizer passes its output gradient to its input unchanged; "How
+ * quantization works": quantized values are rescaled back, beta * q and Xq / s_t).
+ * The matrix products of a training step around these (bf16 inputs, fp32 accumulation)
+ * are plain GEMMs left to the caller's BLAS.
+ *
+ * bitlinear_warmup_lambda: min(step / total, 1) as fp32 (0 for step <= 0, 1 for
+ * total <= 0). */
+float bitlinear_warmup_lambda(int64_t step, int64_t total);
+
+/* W_out[o, k] = bf16(w + lambda * (beta * q - w)), q the code of bitlinear_quantize_weights
+ * for beta = w_scale[0] (so w_scale must come from that call on the same W); every
+ * operation is one fp32 rounding, bf16 rounds to nearest even.
+ *   W       device fp32 [N, K], 16-byte aligned;   w_scale device fp32 [1]
+ *   lambda  in [0, 1];                             W_out   device bf16 bits [N, K], 16-byte aligned */
+bl_status bitlinear_fake_quant_weights(const float* W, int64_t N, int64_t K, const float* w_scale,
+                                       float lambda, uint16_t* W_out, bl_stream_t stream);
+
+/* bitlinear_quantize_acts (same Xq, x_scale), plus
+ *   X_out[t, k] = bf16(y + lambda * (Xq / s_t - y)), y the RMSNorm output (x with
+ *                 BL_NO_NORM), Xq / s_t one fp32 division, every step one fp32 rounding
+ *   x_rinv[t]   = r of the RMSNorm in fp64 (1 with BL_NO_NORM), or NULL
+ *   X_out       device bf16 bits [T, K], 16-byte aligned; x_rinv 8-byte aligned */
+bl_status bitlinear_fake_quant_acts(const float* X, const float* gain, int64_t T, int64_t K,
+                                    float eps, uint32_t flags, float lambda, int8_t* Xq,
+                                    float* x_scale, uint16_t* X_out, double* x_rinv,
+                                    bl_stream_t stream);
+
+/* Backward of y = x * r * g (r from x_rinv), the norm in front of the quantizer; the
+ * quantizer's gradient is the identity, so dY is the gradient with respect to X_out:
+ *   dX[t, k]  = fp32(r g_k dy_k - x_k r^3 (sum_j g_j dy_j x_j) / K), fp64 arithmetic
+ *   dgain[k]  = fp32(sum_t r_t dy_tk x_tk) (fp64), when dgain is not NULL
+ * gain NULL means unit gain. All arrays fp32 [T, K] / [K], 4-byte aligned. */
+bl_status bitlinear_rmsnorm_backward(const float* X, const float* gain, const double* x_rinv,
+                                     const float* dY, int64_t T, int64_t K, float* dX,
+                                     float* dgain, bl_stream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* bitlinear_status_str(bl_status s);
 /* Text of the last failing HIP call made by this thread ("" if none). */

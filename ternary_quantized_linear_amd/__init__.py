@@ -85,6 +85,12 @@ _c_fwsg_scale = _sig("bitlinear_forward_scale_groups",
                      [_P, _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, ctypes.c_int, _P])
 _c_fwg_scale = _sig("bitlinear_forward_grouped_scale_groups",
                     [ctypes.POINTER(_ProjDesc), ctypes.POINTER(_I64), ctypes.c_int, _I64, _P])
+_c_lam = _sig("bitlinear_warmup_lambda", [_I64, _I64], ctypes.c_float)
+_c_fqw = _sig("bitlinear_fake_quant_weights", [_P, _I64, _I64, _P, ctypes.c_float, _P, _P])
+_c_fqa = _sig("bitlinear_fake_quant_acts",
+              [_P, _P, _I64, _I64, ctypes.c_float, ctypes.c_uint32, ctypes.c_float, _P, _P, _P,
+               _P, _P])
+_c_rbw = _sig("bitlinear_rmsnorm_backward", [_P, _P, _P, _P, _I64, _I64, _P, _P, _P])
 _c_str = _sig("bitlinear_status_str", [ctypes.c_int], ctypes.c_char_p)
 _c_err = _sig("bitlinear_last_hip_error", [], ctypes.c_char_p)
 _c_ver = _sig("bitlinear_abi_version", [])
@@ -257,6 +263,29 @@ def prepare_forward_grouped_scale_groups(entries, groups, T):
     return _PreparedScaleGroups(entries, groups, T)
 
 
+def bitlinear_warmup_lambda(step: int, total: int) -> float:
+    return float(_c_lam(int(step), int(total)))
+
+
+def bitlinear_fake_quant_weights(W, w_scale, lam, W_out, stream=None):
+    N, K = W.shape
+    _check(_c_fqw(_ptr(W), N, K, _ptr(w_scale), float(lam), _ptr(W_out), _stream(W, stream)),
+           "bitlinear_fake_quant_weights")
+
+
+def bitlinear_fake_quant_acts(X, gain, eps, flags, lam, Xq, x_scale, X_out, x_rinv, stream=None):
+    T, K = X.shape
+    _check(_c_fqa(_ptr(X), _ptr(gain), T, K, float(eps), int(flags), float(lam), _ptr(Xq),
+                  _ptr(x_scale), _ptr(X_out), _ptr(x_rinv), _stream(X, stream)),
+           "bitlinear_fake_quant_acts")
+
+
+def bitlinear_rmsnorm_backward(X, gain, x_rinv, dY, dX, dgain=None, stream=None):
+    T, K = X.shape
+    _check(_c_rbw(_ptr(X), _ptr(gain), _ptr(x_rinv), _ptr(dY), T, K, _ptr(dX), _ptr(dgain),
+                  _stream(X, stream)), "bitlinear_rmsnorm_backward")
+
+
 class PreparedCall:
     """A grouped ABI call with its descriptor array marshalled once. Calling it
     launches on the current stream at call time (so it can be captured into a graph)."""
@@ -330,6 +359,32 @@ def forward_scale_groups(Xq, x_scale, packed, beta, with_acc: bool = False, kern
     acc = torch.empty((T, N), dtype=torch.int32, device=Xq.device) if with_acc else None
     bitlinear_forward_scale_groups(Xq, x_scale, packed, beta, beta.numel(), Y, acc, kernel)
     return (Y, acc) if with_acc else Y
+
+
+def fake_quant_weights(W: torch.Tensor, beta: torch.Tensor, lam: float) -> torch.Tensor:
+    """W fp32 [N, K] and its beta [1] -> bf16 [N, K] of W + lam * (beta * q - W)."""
+    out = torch.empty(W.shape, dtype=torch.bfloat16, device=W.device)
+    bitlinear_fake_quant_weights(W, beta, lam, out)
+    return out
+
+
+def fake_quant_acts(X: torch.Tensor, lam: float, gain=None, eps: float = 1e-6, flags: int = 0):
+    """X fp32 [T, K] -> (bf16 [T, K] of y + lam * (Xq / s - y), Xq, x_scale, r fp64 [T])."""
+    T, K = X.shape
+    Xq = torch.empty((T, K), dtype=torch.int8, device=X.device)
+    xs = torch.empty(T, dtype=torch.float32, device=X.device)
+    out = torch.empty((T, K), dtype=torch.bfloat16, device=X.device)
+    r = torch.empty(T, dtype=torch.float64, device=X.device)
+    bitlinear_fake_quant_acts(X, gain, eps, flags, lam, Xq, xs, out, r)
+    return out, Xq, xs, r
+
+
+def rmsnorm_backward(X: torch.Tensor, r: torch.Tensor, dY: torch.Tensor, gain=None):
+    """-> (dX fp32 [T, K], dgain fp32 [K] or None)."""
+    dX = torch.empty_like(X)
+    dg = torch.empty(X.shape[1], dtype=torch.float32, device=X.device) if gain is not None else None
+    bitlinear_rmsnorm_backward(X, gain, r, dY, dX, dg)
+    return dX, dg
 
 
 def quantize_weights_sign(W: torch.Tensor):

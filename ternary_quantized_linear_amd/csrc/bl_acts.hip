@@ -26,6 +26,8 @@ struct ActEntry {
   const float* gain;
   int8_t* Xq;
   float* s;
+  uint16_t* xfq;  // training side: bf16 of y + lam * (Xq / s - y), or null
+  double* rinv;   // training side: r per token, or null
   int K;
 };
 
@@ -34,7 +36,28 @@ struct ActArgs {
   int T;
   float eps;
   int no_norm;
+  float lam;
 };
+
+// Training side ([HF-1.58] "Dynamic warm-up quantization", "How quantization works"):
+// y + lam * (q / s - y) with q / s one fp32 division and every step one fp32 rounding
+// (no contraction), then bf16.
+__device__ __forceinline__ uint32_t fq_one(float y, int q, float s, float lam) {
+  const float xd = (float)q / s;
+  const float d = xd - y;
+  const float t = lam * d;
+  return bf16_bits(y + t);
+}
+
+__device__ __forceinline__ int code_of(float v, float s) {
+  return (int)fminf(fmaxf(rintf(v * s), -128.0f), 127.0f);
+}
+
+__device__ __forceinline__ uint2 fq4(float4 y, float s, float lam) {
+  const uint32_t a = fq_one(y.x, code_of(y.x, s), s, lam), b = fq_one(y.y, code_of(y.y, s), s, lam);
+  const uint32_t c = fq_one(y.z, code_of(y.z, s), s, lam), d = fq_one(y.w, code_of(y.w, s), s, lam);
+  return make_uint2(a | (b << 16), c | (d << 16));
+}
 
 // Block-wide double-double sum. Each wave reduces its lanes with DPP into lane 63; after
 // one barrier every wave reduces the per-wave partials itself (DPP over the first NW
@@ -115,7 +138,7 @@ __device__ __forceinline__ uint32_t quant4(float4 y, float s) {
 }
 
 // Row held in registers: lane i owns float4 i, i+NT, ..., i+(VPT-1)NT of the row.
-template <int NT, int VPT>
+template <int NT, int VPT, bool FQ>
 __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   __shared__ double sh_hi[NT / kWave], sh_lo[NT / kWave];
   __shared__ float sh_m[NT / kWave];
@@ -144,6 +167,9 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
     const double r = 1.0 / sqrt(ss / (double)e.K + (double)a.eps);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) v[j] = norm4(v[j], r, gv[j], has_gain);
+    if (FQ && e.rinv && threadIdx.x == 0) e.rinv[t] = r;
+  } else if (FQ && e.rinv && threadIdx.x == 0) {
+    e.rinv[t] = 1.0;
   }
   float m = 0.0f;
 #pragma unroll
@@ -157,11 +183,21 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
     int i = threadIdx.x + j * NT;
     if (i < K4) q4[i] = quant4(v[j], s);
   }
+  if constexpr (FQ) {
+    if (e.xfq) {
+      uint2* f2 = reinterpret_cast<uint2*>(e.xfq + (int64_t)t * e.K);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        int i = threadIdx.x + j * NT;
+        if (i < K4) f2[i] = fq4(v[j], s, a.lam);
+      }
+    }
+  }
   if (threadIdx.x == 0) e.s[t] = s;
 }
 
 // Rows longer than the register budget: three passes over X (L2-resident by then).
-template <int NT>
+template <int NT, bool FQ>
 __global__ __launch_bounds__(NT) void act_quant_stream(ActArgs a) {
   __shared__ double sh_hi[NT / kWave], sh_lo[NT / kWave];
   __shared__ float sh_m[NT / kWave];
@@ -180,6 +216,7 @@ __global__ __launch_bounds__(NT) void act_quant_stream(ActArgs a) {
     block_dd_sum<NT>(hi, lo, sh_hi, sh_lo);
     r = 1.0 / sqrt(hi / (double)e.K + (double)a.eps);
   }
+  if (FQ && e.rinv && threadIdx.x == 0) e.rinv[t] = r;
   auto load_y = [&](int i) -> float4 {
     const float4 f = x4[i];
     if (a.no_norm) return f;
@@ -193,7 +230,13 @@ __global__ __launch_bounds__(NT) void act_quant_stream(ActArgs a) {
   m = block_max<NT>(m, sh_m);
   const float s = 127.0f / fmaxf(m, 1e-5f);
   uint32_t* q4 = reinterpret_cast<uint32_t*>(e.Xq + (int64_t)t * e.K);
-  for (int i = threadIdx.x; i < K4; i += NT) q4[i] = quant4(load_y(i), s);
+  for (int i = threadIdx.x; i < K4; i += NT) {
+    const float4 y = load_y(i);
+    q4[i] = quant4(y, s);
+    if constexpr (FQ) {
+      if (e.xfq) reinterpret_cast<uint2*>(e.xfq + (int64_t)t * e.K)[i] = fq4(y, s, a.lam);
+    }
+  }
   if (threadIdx.x == 0) e.s[t] = s;
 }
 
@@ -201,35 +244,57 @@ __global__ __launch_bounds__(NT) void act_quant_stream(ActArgs a) {
 
 using namespace bl;
 
+namespace {
+
+template <bool FQ>
+hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStream_t stream) {
+  dim3 grid((unsigned)T, (unsigned)count);
+  const int f4 = (maxK + 3) / 4;  // float4 per row
+  if (T <= 64) {
+    // few rows: latency-bound, so spread each row over 1024 lanes
+    if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<1024, 1, FQ>), grid, dim3(1024), 0, stream, a);
+    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<1024, 2, FQ>), grid, dim3(1024), 0, stream, a);
+    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<1024, 4, FQ>), grid, dim3(1024), 0, stream, a);
+    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<1024, 8, FQ>), grid, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);
+    return hipGetLastError();
+  }
+  // many rows: throughput-bound; the smallest register footprint that holds the row
+  if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<256, 8, FQ>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<256, 16, FQ>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ>), grid, dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t bl_launch_quantize_acts(const bl_act_desc* d, int count, int64_t T, float eps,
                                    uint32_t flags, hipStream_t stream) {
   ActArgs a{};
   int maxK = 0;
   for (int i = 0; i < count; ++i) {
-    a.e[i] = ActEntry{d[i].X, d[i].gain, d[i].Xq, d[i].x_scale, (int)d[i].K};
+    a.e[i] = ActEntry{d[i].X, d[i].gain, d[i].Xq, d[i].x_scale, nullptr, nullptr, (int)d[i].K};
     if ((int)d[i].K > maxK) maxK = (int)d[i].K;
   }
   a.T = (int)T;
   a.eps = eps;
   a.no_norm = (flags & BL_NO_NORM) ? 1 : 0;
-  dim3 grid((unsigned)T, (unsigned)count);
-  const int f4 = (maxK + 3) / 4;  // float4 per row
-  if (T <= 64) {
-    // few rows: latency-bound, so spread each row over 1024 lanes
-    if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<1024, 1>), grid, dim3(1024), 0, stream, a);
-    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<1024, 2>), grid, dim3(1024), 0, stream, a);
-    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<1024, 4>), grid, dim3(1024), 0, stream, a);
-    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<1024, 8>), grid, dim3(1024), 0, stream, a);
-    else hipLaunchKernelGGL((act_quant_stream<1024>), grid, dim3(1024), 0, stream, a);
-    return hipGetLastError();
-  }
-  // many rows: throughput-bound; the smallest register footprint that holds the row
-  if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<256, 8>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<256, 16>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16>), grid, dim3(512), 0, stream, a);
-  else hipLaunchKernelGGL((act_quant_stream<1024>), grid, dim3(1024), 0, stream, a);
-  return hipGetLastError();
+  a.lam = 0.0f;
+  return launch_acts<false>(a, maxK, T, count, stream);
+}
+
+hipError_t bl_launch_fake_quant_acts(const float* X, const float* gain, int64_t T, int64_t K,
+                                     float eps, uint32_t flags, float lam, int8_t* Xq, float* xs,
+                                     uint16_t* xfq, double* rinv, hipStream_t stream) {
+  ActArgs a{};
+  a.e[0] = ActEntry{X, gain, Xq, xs, xfq, rinv, (int)K};
+  a.T = (int)T;
+  a.eps = eps;
+  a.no_norm = (flags & BL_NO_NORM) ? 1 : 0;
+  a.lam = lam;
+  return launch_acts<true>(a, (int)K, T, 1, stream);
 }

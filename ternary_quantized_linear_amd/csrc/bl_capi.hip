@@ -301,6 +301,52 @@ bl_status bitlinear_forward_sign(const int8_t* Xq, const float* x_scale, int64_t
   return bitlinear_forward_sign_grouped(&d, 1, T, stream);
 }
 
+float bitlinear_warmup_lambda(int64_t step, int64_t total) {
+  if (total <= 0 || step >= total) return 1.0f;
+  if (step <= 0) return 0.0f;
+  return (float)((double)step / (double)total);
+}
+
+bl_status bitlinear_fake_quant_weights(const float* W, int64_t N, int64_t K, const float* w_scale,
+                                       float lambda, uint16_t* W_out, bl_stream_t stream) {
+  if (!W || !w_scale || !W_out) return BL_ERR_NULL;
+  if (N <= 0 || K <= 0 || K % 4 || N > kMaxRows || N * K > kMaxWeights) return BL_ERR_DIM;
+  if (!(lambda >= 0.0f && lambda <= 1.0f)) return BL_ERR_ARG;
+  if (!aligned16(W) || !aligned16(W_out) || !aligned_n(w_scale, 4)) return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_fake_quant_weights(W, N, K, w_scale, lambda, W_out,
+                                                 (hipStream_t)stream));
+}
+
+bl_status bitlinear_fake_quant_acts(const float* X, const float* gain, int64_t T, int64_t K,
+                                    float eps, uint32_t flags, float lambda, int8_t* Xq,
+                                    float* x_scale, uint16_t* X_out, double* x_rinv,
+                                    bl_stream_t stream) {
+  bl_status s = check_acts(X, gain, T, K, Xq, x_scale);
+  if (s != BL_OK) return s;
+  if (!X_out) return BL_ERR_NULL;
+  if ((flags & ~BL_NO_NORM) != 0u) return BL_ERR_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return BL_ERR_ARG;
+  if (!(lambda >= 0.0f && lambda <= 1.0f)) return BL_ERR_ARG;
+  if (!aligned16(X_out) || (x_rinv && !aligned_n(x_rinv, 8))) return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_fake_quant_acts(X, gain, T, K, eps, flags, lambda, Xq, x_scale, X_out,
+                                              x_rinv, (hipStream_t)stream));
+}
+
+bl_status bitlinear_rmsnorm_backward(const float* X, const float* gain, const double* x_rinv,
+                                     const float* dY, int64_t T, int64_t K, float* dX,
+                                     float* dgain, bl_stream_t stream) {
+  if (!X || !x_rinv || !dY || !dX) return BL_ERR_NULL;
+  if (T <= 0 || K <= 0 || T > kMaxTokens || K > kMaxRows) return BL_ERR_DIM;
+  if (!aligned_n(X, 4) || !aligned_n(dY, 4) || !aligned_n(dX, 4) || !aligned_n(x_rinv, 8) ||
+      (gain && !aligned_n(gain, 4)) || (dgain && !aligned_n(dgain, 4)))
+    return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_rmsnorm_backward(X, gain, x_rinv, dY, T, K, dX, dgain,
+                                               (hipStream_t)stream));
+}
+
 const char* bitlinear_status_str(bl_status s) {
   switch (s) {
     case BL_OK: return "ok";

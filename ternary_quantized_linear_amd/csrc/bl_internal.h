@@ -37,6 +37,16 @@ bool bl_prefill_supports(int T, int K);
 hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream);
 hipError_t bl_launch_generic(const bl_proj_internal* p, int T, hipStream_t stream);
 
+// The training side: fake quantization with the warm-up lambda, RMSNorm backward.
+hipError_t bl_launch_fake_quant_weights(const float* W, int64_t N, int64_t K, const float* w_scale,
+                                        float lam, uint16_t* out, hipStream_t stream);
+hipError_t bl_launch_fake_quant_acts(const float* X, const float* gain, int64_t T, int64_t K,
+                                     float eps, uint32_t flags, float lam, int8_t* Xq, float* xs,
+                                     uint16_t* xfq, double* rinv, hipStream_t stream);
+hipError_t bl_launch_rmsnorm_backward(const float* X, const float* gain, const double* rinv,
+                                      const float* dY, int64_t T, int64_t K, float* dX,
+                                      float* dgain, hipStream_t stream);
+
 // The 1-bit sign variant: weights 8 codes per byte (N rows of K/8 bytes).
 hipError_t bl_launch_quantize_weights_sign(const float* W, int64_t N, int64_t K, uint8_t* P,
                                            float* w_scale, double* w_alpha, void* ws,

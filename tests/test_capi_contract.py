@@ -6,6 +6,8 @@ dereferenced device addresses are passed; a call that passed validation would ne
 GPU, so only failing calls are made here).
 """
 import ctypes
+
+import numpy as np
 import math
 import os
 import re
@@ -54,7 +56,9 @@ def test_header_declares_the_abi():
               "bitlinear_forward_choice", "bitlinear_quantize_weights_sign",
               "bitlinear_forward_sign", "bitlinear_forward_sign_grouped",
               "bitlinear_quantize_weights_scale_groups", "bitlinear_forward_scale_groups",
-              "bitlinear_forward_grouped_scale_groups"]:
+              "bitlinear_forward_grouped_scale_groups", "bitlinear_warmup_lambda",
+              "bitlinear_fake_quant_weights", "bitlinear_fake_quant_acts",
+              "bitlinear_rmsnorm_backward"]:
         assert n in names
 
 
@@ -275,3 +279,34 @@ def test_scale_groups_validation(lib):
     gr = (I64 * 2)(4, 3)
     assert fg(pa, None, 2, 1, None) == BL_ERR_NULL
     assert fg(pa, gr, 2, 1, None) == BL_ERR_ARG  # 3 does not divide 64
+
+
+def test_training_side_validation_and_lambda(lib):
+    lam = lib.bitlinear_warmup_lambda
+    lam.argtypes = [I64, I64]
+    lam.restype = ctypes.c_float
+    assert [lam(t, 1000) for t in (-5, 0, 250, 999, 1000, 5000)] == \
+        [0.0, 0.0, 0.25, np.float32(0.999), 1.0, 1.0]
+    assert lam(3, 0) == 1.0
+    f = lib.bitlinear_fake_quant_weights
+    f.argtypes = [P, I64, I64, P, ctypes.c_float, P, P]
+    f.restype = ctypes.c_int
+    assert f(None, 4, 8, B, 0.5, C, None) == BL_ERR_NULL
+    assert f(A, 4, 6, B, 0.5, C, None) == BL_ERR_DIM
+    assert f(A, 4, 8, B, 1.5, C, None) == BL_ERR_ARG
+    assert f(A, 4, 8, B, -0.1, C, None) == BL_ERR_ARG
+    assert f(A, 4, 8, B, math.nan, C, None) == BL_ERR_ARG
+    assert f(A, 4, 8, B, 0.5, MIS, None) == BL_ERR_ALIGN
+    g = lib.bitlinear_fake_quant_acts
+    g.argtypes = [P, P, I64, I64, ctypes.c_float, ctypes.c_uint32, ctypes.c_float, P, P, P, P, P]
+    g.restype = ctypes.c_int
+    assert g(A, None, 8, 1024, 1e-6, 0, 0.5, B, C, None, None, None) == BL_ERR_NULL
+    assert g(A, None, 8, 1024, 1e-6, 0, 2.0, B, C, D, None, None) == BL_ERR_ARG
+    assert g(A, None, 8, 1024, 1e-6, 0, 0.5, B, C, MIS, None, None) == BL_ERR_ALIGN
+    assert g(A, None, 8, 1024, 1e-6, 0, 0.5, B, C, D, P(0x300004), None) == BL_ERR_ALIGN
+    h = lib.bitlinear_rmsnorm_backward
+    h.argtypes = [P, P, P, P, I64, I64, P, P, P]
+    h.restype = ctypes.c_int
+    assert h(A, None, None, B, 8, 1024, C, None, None) == BL_ERR_NULL
+    assert h(A, None, D, B, 0, 1024, C, None, None) == BL_ERR_DIM
+    assert h(A, None, P(0x300004), B, 8, 1024, C, None, None) == BL_ERR_ALIGN

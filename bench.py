@@ -446,6 +446,51 @@ def run_scale_groups_decode(torch, bl, workloads, G=8, T=1):
             "gemv_frac_hbm": round(gemv_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_train_side(torch, bl, workloads):
+    """Training-side kernels at training shapes: weight fake quantization of the 70B down
+    matrix, activation fake quantization and the RMSNorm backward at T = 2048, K = 4096."""
+    dev = torch.device("cuda:0")
+    N, K = workloads.LLAMA_70B_SWEEP["down"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * workloads.WEIGHT_SIGMA
+    _, beta = bl.quantize_weights(W)
+    Wl = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    g_w = _warm_then_capture(torch, [lambda: bl.bitlinear_fake_quant_weights(W, beta, 0.5, Wl)] * 8)
+    g_w.replay()
+    ms_w = _time_graph(torch, g_w, 1) / 8
+    w_bytes = 6 * N * K + 4
+    del W, Wl
+    torch.cuda.empty_cache()
+    T, K = 2048, 4096
+    X = torch.randn((T, K), generator=gen, device=dev, dtype=torch.float32)
+    dY = torch.randn((T, K), generator=gen, device=dev, dtype=torch.float32)
+    Xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+    xs = torch.empty(T, dtype=torch.float32, device=dev)
+    Xl = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    r = torch.empty(T, dtype=torch.float64, device=dev)
+    dX = torch.empty_like(X)
+    g_a = _warm_then_capture(torch, [lambda: bl.bitlinear_fake_quant_acts(
+        X, None, 1e-6, 0, 0.5, Xq, xs, Xl, r)] * 8)
+    g_a.replay()
+    ms_a = _time_graph(torch, g_a, 1) / 8
+    a_bytes = T * K * (4 + 1 + 2) + T * (4 + 8)
+    g_b = _warm_then_capture(torch, [lambda: bl.bitlinear_rmsnorm_backward(X, None, r, dY, dX)] * 8)
+    g_b.replay()
+    ms_b = _time_graph(torch, g_b, 1) / 8
+    b_bytes = T * K * 12 + T * 8
+    del X, dY, Xq, Xl, dX
+    torch.cuda.empty_cache()
+
+    def rec(ms, b):
+        return {"ms": round(ms, 4), "bytes": b, "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    return {"fake_quant_weights_70b_down": rec(ms_w, w_bytes),
+            "fake_quant_acts_t2048_k4096": rec(ms_a, a_bytes),
+            "rmsnorm_backward_t2048_k4096": rec(ms_b, b_bytes)}
+
+
 def run_calib_copy(torch):
     n = 64 * 1024 * 1024  # 256 MiB of fp32
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -564,6 +609,7 @@ def main():
         line["weight_quant"] = run_weight_quant(torch, bl, workloads)
         line["sign_decode8b"] = run_sign_decode(torch, bl, workloads)
         line["scale_groups_decode8b"] = run_scale_groups_decode(torch, bl, workloads)
+        line["train_side"] = run_train_side(torch, bl, workloads)
     if a.calib_copy:
         line["calib_copy"] = run_calib_copy(torch)
     line["cpu_baseline"] = None if a.no_cpu else run_cpu_baseline(d, workloads)

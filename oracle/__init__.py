@@ -38,6 +38,13 @@ through estimator), in numpy with the roundings written out:
   T4. STE: the gradient of the quantizer output is passed to its input unchanged; the
       RMSNorm backward in fp64: dx = r g dy - x r^3 (sum g dy x) / K, dg = sum_t r dy x
 
+and BitDelta (a base model plus per-model 1-bit deltas, numpy):
+
+  D1. delta = fp32(W_fine - W_base); alpha = fp32(exact sum |delta| / (N*M))
+  D2. codes = +1 where delta > 0, else -1; eight per byte as in S4; a batch of B models
+      interleaves the codes per 16-code group (2 bytes per model)
+  D3. Y[i, n] = sum_k base[n,k] x[i,k] + alpha_i sum_k c_i[n,k] x[i,k], in fp64
+
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (brute force in exact rationals, library routines, closed forms, invariants and the
 worked examples under ``tests/golden/``).
@@ -472,3 +479,42 @@ def rmsnorm_backward(X, gain, r, dY):
 def math_fsum(v):
     import math
     return math.fsum(np.asarray(v, np.float64).tolist())
+
+
+# ---------------------------------------------------------------- BitDelta (numpy)
+# [BitDelta] "BitDelta: Your Fine-Tune May Only Be Worth One Bit": Eq. (1) the delta of
+# a fine-tuned model is approximated by alpha times its sign; Eq. (2) Sign(W) = +1 for
+# W > 0 and -1 otherwise; Eq. (4) alpha = the mean of |delta| over all n*m entries, the
+# minimizer of the L2 error of Eq. (3); Eq. (6) the fine-tuned product is the base
+# product plus the 1-bit delta product.
+
+def bitdelta_compress(W_fine, W_base_bf16):
+    """W_fine fp32 [N, M], base as bf16 bits [N, M] -> (sign bits [N, M/8] (S4 layout),
+    alpha fp32, codes int8 [N, M])."""
+    W_fine = _f32(W_fine)
+    base = bf16_to_f32(W_base_bf16)
+    delta = (W_fine - base).astype(np.float32)
+    codes = np.where(delta > 0, 1, -1).astype(np.int8)
+    alpha = np.float32(abs_sum(delta) / float(delta.size))
+    return pack1(codes), alpha, codes
+
+
+def bitdelta_interleave(bits_list):
+    """Per-model sign bits [N, M/8] (B of them) -> the batched layout [N, M/16, B, 2]."""
+    B = len(bits_list)
+    N, mb = bits_list[0].shape
+    out = np.empty((N, mb // 2, B, 2), np.uint8)
+    for i, b in enumerate(bits_list):
+        out[:, :, i, :] = np.asarray(b, np.uint8).reshape(N, mb // 2, 2)
+    return out.reshape(N, -1)
+
+
+def bitdelta_forward(W_base_bf16, codes_list, alphas, X):
+    """Y [B, N] fp32 = base . x_i + alpha_i * codes_i . x_i, computed in fp64."""
+    base = bf16_to_f32(W_base_bf16).astype(np.float64)
+    X = np.asarray(X, np.float64)
+    B = X.shape[0]
+    Y = np.empty((B, base.shape[0]), np.float64)
+    for i in range(B):
+        Y[i] = base @ X[i] + float(alphas[i]) * (np.asarray(codes_list[i], np.float64) @ X[i])
+    return Y.astype(np.float32)

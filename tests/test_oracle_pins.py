@@ -663,3 +663,65 @@ def test_rmsnorm_backward_against_autograd():
     dX, dg = oracle.rmsnorm_backward(X, g, rr, dY)
     assert np.allclose(dX, xt.grad.numpy(), rtol=1e-6, atol=1e-7)
     assert np.allclose(dg, gt.grad.numpy(), rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------- BitDelta
+
+def test_golden_bitdelta():
+    g = load("bitdelta.txt")
+    base = oracle.bf16_bits(np.array(g["W_base"], np.float32))
+    bits, alpha, codes = oracle.bitdelta_compress(np.array(g["W_fine"], np.float32), base)
+    assert alpha == g["alpha"] and codes.tolist() == g["codes"] and bits.tolist() == g["bits"]
+    y = oracle.bitdelta_forward(base, [codes], [alpha], np.array(g["x"], np.float32))
+    assert y.tolist() == g["y"]
+
+
+def test_bitdelta_alpha_is_l2_optimal():
+    # [BitDelta] Eq. (3)-(4): with S = Sign(delta), ||delta - a S||^2 is smallest at
+    # a = mean |delta| (closed form sum(delta * S) / sum(S * S), and a numerical check)
+    r = np.random.default_rng(31)
+    base = oracle.bf16_bits((r.standard_normal((64, 256)) * 0.02).astype(np.float32))
+    fine = (oracle.bf16_to_f32(base) + r.standard_normal((64, 256)).astype(np.float32) * 0.001
+            ).astype(np.float32)
+    bits, alpha, codes = oracle.bitdelta_compress(fine, base)
+    delta = (fine - oracle.bf16_to_f32(base)).astype(np.float64).ravel()
+    s = codes.astype(np.float64).ravel()
+    a_star = float(np.dot(delta, s) / np.dot(s, s))
+    assert abs(a_star - float(alpha)) <= 2.0 ** -23 * float(alpha)
+
+    def err(a):
+        return float(np.sum((delta - a * s) ** 2))
+
+    for d in (1e-2, 1e-4):
+        assert err(float(alpha)) <= err(float(alpha) * (1 + d))
+        assert err(float(alpha)) <= err(float(alpha) * (1 - d))
+
+
+def test_bitdelta_interleave_and_forward_dense():
+    # the batched layout holds each model's 2-byte groups side by side; the forward
+    # equals the dense fp64 product with the dequantized fine-tuned matrices
+    r = np.random.default_rng(33)
+    B, N, M = 3, 20, 64
+    base = oracle.bf16_bits((r.standard_normal((N, M)) * 0.02).astype(np.float32))
+    bits, alphas, codes = [], [], []
+    for i in range(B):
+        fine = (oracle.bf16_to_f32(base) + r.standard_normal((N, M)).astype(np.float32) * 0.002
+                ).astype(np.float32)
+        b, a, c = oracle.bitdelta_compress(fine, base)
+        bits.append(b)
+        alphas.append(a)
+        codes.append(c)
+    inter = oracle.bitdelta_interleave(bits)
+    assert inter.shape == (N, M // 8 * B)
+    for i in range(B):
+        for n in range(N):
+            for j in range(M // 16):
+                assert inter[n, (j * B + i) * 2] == bits[i][n, 2 * j]
+                assert inter[n, (j * B + i) * 2 + 1] == bits[i][n, 2 * j + 1]
+    X = r.standard_normal((B, M)).astype(np.float32)
+    Y = oracle.bitdelta_forward(base, codes, alphas, X)
+    for i in range(B):
+        dense = oracle.bf16_to_f32(base).astype(np.float64) + float(alphas[i]) * \
+            oracle.unpack1(bits[i], M).astype(np.float64)
+        assert np.allclose(Y[i].astype(np.float64), dense @ X[i].astype(np.float64),
+                           rtol=1e-6, atol=1e-7)

@@ -290,6 +290,35 @@ bl_status bitlinear_rmsnorm_backward(const float* X, const float* gain, const do
                                      const float* dY, int64_t T, int64_t K, float* dX,
                                      float* dgain, bl_stream_t stream);
 
+/* ---------------------------------------------------------------- BitDelta
+ *
+ * One base weight matrix shared by B fine-tuned models, each model stored as a 1-bit
+ * delta ([BitDelta] "BitDelta: Your Fine-Tune May Only Be Worth One Bit": Eq. (1)
+ * delta ~ alpha * Sign(delta), Eq. (2) Sign(W) = +1 for W > 0 and -1 otherwise, Eq. (4)
+ * alpha = mean |delta|, Eq. (6) y_i = W_base x_i + alpha_i Sign(delta_i) x_i).
+ * Shapes: W_base bf16 bits [N, M]; 1 <= B <= 8 models; M % 16 == 0, 16 <= M <= 8192,
+ * N * M * 2 < 2^31 (else BL_ERR_DIM).
+ * D (the batched deltas): uint8 [N, M/8 * B], row n, 16-code group j, model i at bytes
+ * ((n * M/16 + j) * B + i) * 2; bit c of the pair is code 16j + c, set for +1.
+ *
+ * bitlinear_bitdelta_compress: model `model`'s signs and scale from W_fine (fp32 [N, M],
+ * 16-byte aligned): delta = fp32(W_fine - W_base); alpha[model] = fp32((exact sum of
+ * |delta|, rounded once to fp64) / (N*M)); its bit pairs written into D (16-byte
+ * aligned); other models' bytes untouched. workspace as for bitlinear_quantize_weights. */
+bl_status bitlinear_bitdelta_compress(const float* W_fine, const uint16_t* W_base, int64_t N,
+                                      int64_t M, int B, int model, uint8_t* D, float* alpha,
+                                      void* workspace, size_t workspace_bytes,
+                                      bl_stream_t stream);
+
+/* Y[i, n] = sum_k base[n, k] X[i, k] + alpha_i * sum_k c_i[n, k] X[i, k] for the B
+ * tokens X fp32 [B, M] (16-byte aligned), Y fp32 [B, N]. fp32 arithmetic: the base part
+ * with FMAs per 16 codes, the delta part as 2 * (sum of x where the bit is set) - sum x,
+ * partial sums added across lanes and waves; the order of the final float additions
+ * depends on scheduling, so the last bits of Y may vary from call to call. */
+bl_status bitlinear_bitdelta_forward(const uint16_t* W_base, const uint8_t* D, const float* alpha,
+                                     const float* X, int64_t N, int64_t M, int B, float* Y,
+                                     bl_stream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* bitlinear_status_str(bl_status s);
 /* Text of the last failing HIP call made by this thread ("" if none). */

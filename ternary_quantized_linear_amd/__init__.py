@@ -91,6 +91,10 @@ _c_fqa = _sig("bitlinear_fake_quant_acts",
               [_P, _P, _I64, _I64, ctypes.c_float, ctypes.c_uint32, ctypes.c_float, _P, _P, _P,
                _P, _P])
 _c_rbw = _sig("bitlinear_rmsnorm_backward", [_P, _P, _P, _P, _I64, _I64, _P, _P, _P])
+_c_bdc = _sig("bitlinear_bitdelta_compress",
+              [_P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P])
+_c_bdf = _sig("bitlinear_bitdelta_forward",
+              [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P])
 _c_str = _sig("bitlinear_status_str", [ctypes.c_int], ctypes.c_char_p)
 _c_err = _sig("bitlinear_last_hip_error", [], ctypes.c_char_p)
 _c_ver = _sig("bitlinear_abi_version", [])
@@ -286,6 +290,21 @@ def bitlinear_rmsnorm_backward(X, gain, x_rinv, dY, dX, dgain=None, stream=None)
                   _stream(X, stream)), "bitlinear_rmsnorm_backward")
 
 
+def bitlinear_bitdelta_compress(W_fine, W_base, B, model, D, alpha, workspace, stream=None):
+    N, M = W_fine.shape
+    _check(_c_bdc(_ptr(W_fine), _ptr(W_base), N, M, int(B), int(model), _ptr(D), _ptr(alpha),
+                  _ptr(workspace),
+                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                  _stream(W_fine, stream)), "bitlinear_bitdelta_compress")
+
+
+def bitlinear_bitdelta_forward(W_base, D, alpha, X, Y, stream=None):
+    N, M = W_base.shape
+    B = X.shape[0]
+    _check(_c_bdf(_ptr(W_base), _ptr(D), _ptr(alpha), _ptr(X), N, M, int(B), _ptr(Y),
+                  _stream(X, stream)), "bitlinear_bitdelta_forward")
+
+
 class PreparedCall:
     """A grouped ABI call with its descriptor array marshalled once. Calling it
     launches on the current stream at call time (so it can be captured into a graph)."""
@@ -385,6 +404,27 @@ def rmsnorm_backward(X: torch.Tensor, r: torch.Tensor, dY: torch.Tensor, gain=No
     dg = torch.empty(X.shape[1], dtype=torch.float32, device=X.device) if gain is not None else None
     bitlinear_rmsnorm_backward(X, gain, r, dY, dX, dg)
     return dX, dg
+
+
+def bitdelta_compress(W_fines, W_base: torch.Tensor):
+    """B fine-tuned fp32 [N, M] matrices and the base (bf16 [N, M]) -> (batched sign bits
+    uint8 [N, M/8 * B], alpha fp32 [B])."""
+    B = len(W_fines)
+    N, M = W_base.shape
+    dev = W_base.device
+    D = torch.zeros((N, M // 8 * B), dtype=torch.uint8, device=dev)
+    alpha = torch.empty(B, dtype=torch.float32, device=dev)
+    ws = torch.empty(bitlinear_weight_workspace_bytes(N, M), dtype=torch.uint8, device=dev)
+    for i, Wf in enumerate(W_fines):
+        bitlinear_bitdelta_compress(Wf, W_base.view(torch.int16), B, i, D, alpha, ws)
+    return D, alpha
+
+
+def bitdelta_forward(W_base: torch.Tensor, D, alpha, X: torch.Tensor) -> torch.Tensor:
+    """Y fp32 [B, N] = W_base x_i + alpha_i Sign(delta_i) x_i for X fp32 [B, M]."""
+    Y = torch.empty((X.shape[0], W_base.shape[0]), dtype=torch.float32, device=X.device)
+    bitlinear_bitdelta_forward(W_base.view(torch.int16), D, alpha, X, Y)
+    return Y
 
 
 def quantize_weights_sign(W: torch.Tensor):

@@ -347,6 +347,35 @@ bl_status bitlinear_rmsnorm_backward(const float* X, const float* gain, const do
                                                (hipStream_t)stream));
 }
 
+bl_status bitlinear_bitdelta_compress(const float* W_fine, const uint16_t* W_base, int64_t N,
+                                      int64_t M, int B, int model, uint8_t* D, float* alpha,
+                                      void* workspace, size_t workspace_bytes,
+                                      bl_stream_t stream) {
+  if (!W_fine || !W_base || !D || !alpha) return BL_ERR_NULL;
+  if (!bl_bitdelta_supports(N, M, B)) return BL_ERR_DIM;
+  if (model < 0 || model >= B) return BL_ERR_ARG;
+  if (!workspace || workspace_bytes < bitlinear_weight_workspace_bytes(N, M))
+    return BL_ERR_WORKSPACE;
+  if (!aligned16(W_fine) || !aligned16(W_base) || !aligned16(D) || !aligned16(workspace) ||
+      !aligned_n(alpha, 4))
+    return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_bitdelta_compress(W_fine, W_base, N, M, B, model, D, alpha + model,
+                                                workspace, (hipStream_t)stream));
+}
+
+bl_status bitlinear_bitdelta_forward(const uint16_t* W_base, const uint8_t* D, const float* alpha,
+                                     const float* X, int64_t N, int64_t M, int B, float* Y,
+                                     bl_stream_t stream) {
+  if (!W_base || !D || !alpha || !X || !Y) return BL_ERR_NULL;
+  if (!bl_bitdelta_supports(N, M, B)) return BL_ERR_DIM;
+  if (!aligned16(W_base) || !aligned16(X) || !aligned_n(D, 4) || !aligned_n(alpha, 4) ||
+      !aligned_n(Y, 4))
+    return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_bitdelta(W_base, D, alpha, X, Y, N, M, B, (hipStream_t)stream));
+}
+
 const char* bitlinear_status_str(bl_status s) {
   switch (s) {
     case BL_OK: return "ok";

@@ -65,10 +65,12 @@ __device__ __forceinline__ void split_abs(float x, unsigned& m, int& sh) {
 }
 
 // SIGNED: a second accumulator (neg) collects |w| of the negative weights.
-template <bool SIGNED>
+// DIFF: the values summed are fp32(w - base), base given as bf16 bits (BitDelta deltas).
+template <bool SIGNED, bool DIFF = false>
 __global__ __launch_bounds__(kSumThreads) void wq_abssum(const float4* __restrict__ W4,
                                                          int64_t n4,
-                                                         unsigned long long* __restrict__ ws) {
+                                                         unsigned long long* __restrict__ ws,
+                                                         const uint2* __restrict__ base4) {
   constexpr int ND = SIGNED ? 2 * kDigits : kDigits;
   __shared__ unsigned long long dig[ND];
   unsigned long long* neg = dig + kDigits;  // used only when SIGNED
@@ -85,6 +87,13 @@ __global__ __launch_bounds__(kSumThreads) void wq_abssum(const float4* __restric
     for (int j = 0; j < 4; ++j) {
       int64_t i = c * 256 + j * 64 + lane;
       float4 f = i < n4 ? W4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (DIFF) {
+        const uint2 b = i < n4 ? base4[i] : make_uint2(0u, 0u);
+        f.x = f.x - __uint_as_float(b.x << 16);
+        f.y = f.y - __uint_as_float(b.x & 0xFFFF0000u);
+        f.z = f.z - __uint_as_float(b.y << 16);
+        f.w = f.w - __uint_as_float(b.y & 0xFFFF0000u);
+      }
       v[4 * j + 0] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
     }
     unsigned m[16];
@@ -301,6 +310,28 @@ __global__ void wq_pack1_tail(const float* __restrict__ W, int64_t n,
   P[byte] = (uint8_t)v;
 }
 
+// BitDelta signs ([BitDelta] Eq. (2): +1 where delta > 0, else -1) of one model into the
+// batched layout: row n, 16-code group j, model `model` of B: 2 bytes at
+// ((n * (M/16) + j) * B + model) * 2, bit i of the pair = code 16j + i.
+__global__ __launch_bounds__(256) void bd_pack(const float4* __restrict__ fine4,
+                                               const uint2* __restrict__ base4, int64_t groups,
+                                               int B, int model, uint16_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += stride) {
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = fine4[4 * g + q];
+      const uint2 b = base4[4 * g + q];
+      const float d[4] = {f.x - __uint_as_float(b.x << 16), f.y - __uint_as_float(b.x & 0xFFFF0000u),
+                          f.z - __uint_as_float(b.y << 16), f.w - __uint_as_float(b.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bits |= (d[c] > 0.0f ? 1u : 0u) << (4 * q + c);
+    }
+    out[g * B + model] = (uint16_t)bits;
+  }
+}
+
 }  // namespace bl
 
 using namespace bl;
@@ -333,8 +364,8 @@ hipError_t bl_launch_quantize_weights(const float* W, int64_t N, int64_t K, uint
   const int64_t n4 = n / 4;  // K % 4 == 0, so n % 4 == 0
   const int64_t blocks = sum_blocks(n4);
   auto* dig = static_cast<unsigned long long*>(ws);
-  hipLaunchKernelGGL(wq_abssum<false>, dim3((unsigned)blocks), dim3(kSumThreads), 0, stream,
-                     reinterpret_cast<const float4*>(W), n4, dig);
+  hipLaunchKernelGGL((wq_abssum<false, false>), dim3((unsigned)blocks), dim3(kSumThreads), 0,
+                     stream, reinterpret_cast<const float4*>(W), n4, dig, (const uint2*)nullptr);
   hipLaunchKernelGGL(wq_finalize<false>, dim3(1), dim3(kSumThreads), 0, stream, dig, (int)blocks,
                      n, w_scale, w_gamma, (double*)nullptr, (double*)nullptr);
   int64_t pblocks = (n4 + 1023) / 1024;
@@ -352,8 +383,8 @@ hipError_t bl_launch_quantize_weights_sign(const float* W, int64_t N, int64_t K,
   const int64_t n4 = n / 4;  // K % 8 == 0
   const int64_t blocks = sum_blocks(n4);
   auto* dig = static_cast<unsigned long long*>(ws);
-  hipLaunchKernelGGL(wq_abssum<true>, dim3((unsigned)blocks), dim3(kSumThreads), 0, stream,
-                     reinterpret_cast<const float4*>(W), n4, dig);
+  hipLaunchKernelGGL((wq_abssum<true, false>), dim3((unsigned)blocks), dim3(kSumThreads), 0,
+                     stream, reinterpret_cast<const float4*>(W), n4, dig, (const uint2*)nullptr);
   hipLaunchKernelGGL(wq_finalize<true>, dim3(1), dim3(kSumThreads), 0, stream, dig, (int)blocks,
                      n, w_scale, (double*)nullptr, alpha_slot(ws), w_alpha);
   const int64_t ndw = n / 32;  // packed dwords; K % 8 == 0 but n may not be a multiple of 32
@@ -368,5 +399,26 @@ hipError_t bl_launch_quantize_weights_sign(const float* W, int64_t N, int64_t K,
     // the last few bytes (n % 32 = 8, 16 or 24 codes): one thread per byte
     hipLaunchKernelGGL(wq_pack1_tail, dim3(1), dim3(64), 0, stream, W, n, alpha_slot(ws), P);
   }
+  return hipGetLastError();
+}
+
+hipError_t bl_launch_bitdelta_compress(const float* W_fine, const uint16_t* W_base, int64_t N,
+                                       int64_t M, int B, int model, uint8_t* D, float* alpha,
+                                       void* ws, hipStream_t stream) {
+  const int64_t n = N * M;
+  const int64_t n4 = n / 4;  // M % 16 == 0
+  const int64_t blocks = sum_blocks(n4);
+  auto* dig = static_cast<unsigned long long*>(ws);
+  hipLaunchKernelGGL((wq_abssum<false, true>), dim3((unsigned)blocks), dim3(kSumThreads), 0, stream,
+                     reinterpret_cast<const float4*>(W_fine), n4, dig,
+                     reinterpret_cast<const uint2*>(W_base));
+  hipLaunchKernelGGL(wq_finalize<false>, dim3(1), dim3(kSumThreads), 0, stream, dig, (int)blocks,
+                     n, alpha, (double*)nullptr, (double*)nullptr, (double*)nullptr);
+  const int64_t groups = n / 16;
+  int64_t pblocks = (groups + 255) / 256;
+  if (pblocks > 4096) pblocks = 4096;
+  hipLaunchKernelGGL(bd_pack, dim3((unsigned)pblocks), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(W_fine), reinterpret_cast<const uint2*>(W_base),
+                     groups, B, model, reinterpret_cast<uint16_t*>(D));
   return hipGetLastError();
 }

@@ -58,7 +58,8 @@ def test_header_declares_the_abi():
               "bitlinear_quantize_weights_scale_groups", "bitlinear_forward_scale_groups",
               "bitlinear_forward_grouped_scale_groups", "bitlinear_warmup_lambda",
               "bitlinear_fake_quant_weights", "bitlinear_fake_quant_acts",
-              "bitlinear_rmsnorm_backward"]:
+              "bitlinear_rmsnorm_backward", "bitlinear_bitdelta_compress",
+              "bitlinear_bitdelta_forward"]:
         assert n in names
 
 
@@ -310,3 +311,25 @@ def test_training_side_validation_and_lambda(lib):
     assert h(A, None, None, B, 8, 1024, C, None, None) == BL_ERR_NULL
     assert h(A, None, D, B, 0, 1024, C, None, None) == BL_ERR_DIM
     assert h(A, None, P(0x300004), B, 8, 1024, C, None, None) == BL_ERR_ALIGN
+
+
+def test_bitdelta_validation(lib):
+    c = lib.bitlinear_bitdelta_compress
+    c.argtypes = [P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_size_t, P]
+    c.restype = ctypes.c_int
+    lib.bitlinear_weight_workspace_bytes.argtypes = [I64, I64]
+    lib.bitlinear_weight_workspace_bytes.restype = ctypes.c_size_t
+    ws = lib.bitlinear_weight_workspace_bytes(64, 1024)
+    assert c(None, B, 64, 1024, 8, 0, C, D, E, ws, None) == BL_ERR_NULL
+    assert c(A, B, 64, 1000, 8, 0, C, D, E, ws, None) == BL_ERR_DIM     # M % 16
+    assert c(A, B, 64, 16384, 8, 0, C, D, E, ws, None) == BL_ERR_DIM    # M <= 8192
+    assert c(A, B, 64, 1024, 9, 0, C, D, E, ws, None) == BL_ERR_DIM     # B <= 8
+    assert c(A, B, 64, 1024, 8, 8, C, D, E, ws, None) == BL_ERR_ARG     # model < B
+    assert c(A, B, 64, 1024, 8, 0, C, D, E, ws - 1, None) == BL_ERR_WORKSPACE
+    assert c(A, B, 64, 1024, 8, 0, MIS, D, E, ws, None) == BL_ERR_ALIGN
+    f = lib.bitlinear_bitdelta_forward
+    f.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P]
+    f.restype = ctypes.c_int
+    assert f(A, B, C, None, 64, 1024, 8, E, None) == BL_ERR_NULL
+    assert f(A, B, C, D, 64, 1024, 0, E, None) == BL_ERR_DIM
+    assert f(A, B, C, MIS, 64, 1024, 8, E, None) == BL_ERR_ALIGN

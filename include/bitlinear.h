@@ -298,13 +298,14 @@ bl_status bitlinear_rmsnorm_backward(const float* X, const float* gain, const do
  * alpha = mean |delta|, Eq. (6) y_i = W_base x_i + alpha_i Sign(delta_i) x_i).
  * Shapes: W_base bf16 bits [N, M]; 1 <= B <= 8 models; M % 16 == 0, 16 <= M <= 8192,
  * N * M * 2 < 2^31 (else BL_ERR_DIM).
- * D (the batched deltas): uint8 [N, M/8 * B], row n, 16-code group j, model i at bytes
- * ((n * M/16 + j) * B + i) * 2; bit c of the pair is code 16j + c, set for +1.
+ * D (the batched deltas): uint8 [N, M], 16-byte aligned: row n, 16-code group j, model
+ * slot i (of 8) at bytes ((n * M/16 + j) * 8 + i) * 2; bit c of the pair is code 16j + c,
+ * set for +1; slots >= B are not read.
  *
  * bitlinear_bitdelta_compress: model `model`'s signs and scale from W_fine (fp32 [N, M],
  * 16-byte aligned): delta = fp32(W_fine - W_base); alpha[model] = fp32((exact sum of
  * |delta|, rounded once to fp64) / (N*M)); its bit pairs written into D (16-byte
- * aligned); other models' bytes untouched. workspace as for bitlinear_quantize_weights. */
+ * aligned); other slots' bytes untouched. workspace as for bitlinear_quantize_weights. */
 bl_status bitlinear_bitdelta_compress(const float* W_fine, const uint16_t* W_base, int64_t N,
                                       int64_t M, int B, int model, uint8_t* D, float* alpha,
                                       void* workspace, size_t workspace_bytes,

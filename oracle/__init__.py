@@ -41,8 +41,8 @@ through estimator), in numpy with the roundings written out:
 and BitDelta (a base model plus per-model 1-bit deltas, numpy):
 
   D1. delta = fp32(W_fine - W_base); alpha = fp32(exact sum |delta| / (N*M))
-  D2. codes = +1 where delta > 0, else -1; eight per byte as in S4; a batch of B models
-      interleaves the codes per 16-code group (2 bytes per model)
+  D2. codes = +1 where delta > 0, else -1; eight per byte as in S4; a batch of up to 8
+      models interleaves the codes per 16-code group (2 bytes per model slot, 8 slots)
   D3. Y[i, n] = sum_k base[n,k] x[i,k] + alpha_i sum_k c_i[n,k] x[i,k], in fp64
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
@@ -500,10 +500,10 @@ def bitdelta_compress(W_fine, W_base_bf16):
 
 
 def bitdelta_interleave(bits_list):
-    """Per-model sign bits [N, M/8] (B of them) -> the batched layout [N, M/16, B, 2]."""
-    B = len(bits_list)
+    """Per-model sign bits [N, M/8] (B <= 8 of them) -> the batched layout [N, M/16, 8, 2]
+    (slots past B zero)."""
     N, mb = bits_list[0].shape
-    out = np.empty((N, mb // 2, B, 2), np.uint8)
+    out = np.zeros((N, mb // 2, 8, 2), np.uint8)
     for i, b in enumerate(bits_list):
         out[:, :, i, :] = np.asarray(b, np.uint8).reshape(N, mb // 2, 2)
     return out.reshape(N, -1)

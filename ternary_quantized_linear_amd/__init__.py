@@ -407,12 +407,12 @@ def rmsnorm_backward(X: torch.Tensor, r: torch.Tensor, dY: torch.Tensor, gain=No
 
 
 def bitdelta_compress(W_fines, W_base: torch.Tensor):
-    """B fine-tuned fp32 [N, M] matrices and the base (bf16 [N, M]) -> (batched sign bits
-    uint8 [N, M/8 * B], alpha fp32 [B])."""
+    """B (<= 8) fine-tuned fp32 [N, M] matrices and the base (bf16 [N, M]) -> (batched sign
+    bits uint8 [N, M], alpha fp32 [B])."""
     B = len(W_fines)
     N, M = W_base.shape
     dev = W_base.device
-    D = torch.zeros((N, M // 8 * B), dtype=torch.uint8, device=dev)
+    D = torch.zeros((N, M), dtype=torch.uint8, device=dev)
     alpha = torch.empty(B, dtype=torch.float32, device=dev)
     ws = torch.empty(bitlinear_weight_workspace_bytes(N, M), dtype=torch.uint8, device=dev)
     for i, Wf in enumerate(W_fines):

@@ -8,10 +8,10 @@
 // this for B = 8 models at N = M = 8192 (one base matrix and B deltas read per token
 // batch, instead of B full matrices).
 //
-// Layout: W_base bf16 [N, M] row-major; the B models' sign bits interleaved per 16-code
-// group: row n, group j, model i at bytes ((n * M/16 + j) * B + i) * 2 (bit c = code
-// 16j + c, set for +1), so that one 16-byte load brings a lane all eight models' bits for
-// its 16 codes; X fp32 [B, M]; Y fp32 [B, N].
+// Layout: W_base bf16 [N, M] row-major; the models' sign bits interleaved per 16-code
+// group in 8 slots: row n, group j, model i at bytes ((n * M/16 + j) * 8 + i) * 2 (bit
+// c = code 16j + c, set for +1; slots >= B unused), so that one aligned 16-byte load
+// brings a lane every model's bits for its 16 codes; X fp32 [B, M]; Y fp32 [B, N].
 //
 // Kernel: a workgroup of 8 waves takes rows n = w, w + nwg, ...; wave s owns codes
 // [1024 s, 1024 s + 1024) of every row (M <= 8192), 16 per lane, and keeps those 16
@@ -101,8 +101,7 @@ __global__ __launch_bounds__(kBdThreads) void bitdelta_kernel(BdArgs a) {
                                                       (int)((uint32_t)a.N * (uint32_t)a.M * 2u),
                                                       0x00020000);
   const BdRsrc dr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.D), 0,
-                                                      (int)((uint32_t)a.N * (uint32_t)(a.M / 16) *
-                                                            (uint32_t)B * 2u),
+                                                      (int)((uint32_t)a.N * (uint32_t)a.M),
                                                       0x00020000);
   const int wgl = blockIdx.x;
   uint4 wb[kBdDepth][2], wd[kBdDepth];
@@ -111,8 +110,7 @@ __global__ __launch_bounds__(kBdThreads) void bitdelta_kernel(BdArgs a) {
     const int n = wgl + fr * a.nwg;
     const bool ok = on && n < a.N;
     const uint32_t bo = ok ? ((uint32_t)n * (uint32_t)a.M + (uint32_t)k0) * 2u : kBdOob;
-    const uint32_t dof = ok ? (((uint32_t)n * (uint32_t)(a.M / 16) + (uint32_t)(k0 / 16)) *
-                               (uint32_t)B) * 2u
+    const uint32_t dof = ok ? ((uint32_t)n * (uint32_t)(a.M / 16) + (uint32_t)(k0 / 16)) * 16u
                             : kBdOob;
     typedef int v4i __attribute__((ext_vector_type(4)));
     const v4i b0 = __builtin_amdgcn_raw_buffer_load_b128(br, bo, 0, 2);

@@ -360,7 +360,7 @@ bl_status bitlinear_bitdelta_compress(const float* W_fine, const uint16_t* W_bas
       !aligned_n(alpha, 4))
     return BL_ERR_ALIGN;
   (void)hipGetLastError();
-  return hip_status(bl_launch_bitdelta_compress(W_fine, W_base, N, M, B, model, D, alpha + model,
+  return hip_status(bl_launch_bitdelta_compress(W_fine, W_base, N, M, model, D, alpha + model,
                                                 workspace, (hipStream_t)stream));
 }
 
@@ -369,7 +369,7 @@ bl_status bitlinear_bitdelta_forward(const uint16_t* W_base, const uint8_t* D, c
                                      bl_stream_t stream) {
   if (!W_base || !D || !alpha || !X || !Y) return BL_ERR_NULL;
   if (!bl_bitdelta_supports(N, M, B)) return BL_ERR_DIM;
-  if (!aligned16(W_base) || !aligned16(X) || !aligned_n(D, 4) || !aligned_n(alpha, 4) ||
+  if (!aligned16(W_base) || !aligned16(X) || !aligned16(D) || !aligned_n(alpha, 4) ||
       !aligned_n(Y, 4))
     return BL_ERR_ALIGN;
   (void)hipGetLastError();

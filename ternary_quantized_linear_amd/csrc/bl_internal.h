@@ -39,8 +39,8 @@ hipError_t bl_launch_generic(const bl_proj_internal* p, int T, hipStream_t strea
 
 // BitDelta: base bf16 [N, M] plus B interleaved 1-bit deltas, one token per model.
 hipError_t bl_launch_bitdelta_compress(const float* W_fine, const uint16_t* W_base, int64_t N,
-                                       int64_t M, int B, int model, uint8_t* D, float* alpha,
-                                       void* ws, hipStream_t stream);
+                                       int64_t M, int model, uint8_t* D, float* alpha, void* ws,
+                                       hipStream_t stream);
 bool bl_bitdelta_supports(int64_t N, int64_t M, int B);
 hipError_t bl_launch_bitdelta(const uint16_t* base, const uint8_t* D, const float* alpha,
                               const float* X, float* Y, int64_t N, int64_t M, int B,

@@ -311,11 +311,11 @@ __global__ void wq_pack1_tail(const float* __restrict__ W, int64_t n,
 }
 
 // BitDelta signs ([BitDelta] Eq. (2): +1 where delta > 0, else -1) of one model into the
-// batched layout: row n, 16-code group j, model `model` of B: 2 bytes at
-// ((n * (M/16) + j) * B + model) * 2, bit i of the pair = code 16j + i.
+// batched layout: row n, 16-code group j, model slot `model` of 8: 2 bytes at
+// ((n * (M/16) + j) * 8 + model) * 2, bit i of the pair = code 16j + i.
 __global__ __launch_bounds__(256) void bd_pack(const float4* __restrict__ fine4,
                                                const uint2* __restrict__ base4, int64_t groups,
-                                               int B, int model, uint16_t* __restrict__ out) {
+                                               int model, uint16_t* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += stride) {
     uint32_t bits = 0u;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void bd_pack(const float4* __restrict__ fine4,
 #pragma unroll
       for (int c = 0; c < 4; ++c) bits |= (d[c] > 0.0f ? 1u : 0u) << (4 * q + c);
     }
-    out[g * B + model] = (uint16_t)bits;
+    out[g * 8 + model] = (uint16_t)bits;
   }
 }
 
@@ -403,8 +403,8 @@ hipError_t bl_launch_quantize_weights_sign(const float* W, int64_t N, int64_t K,
 }
 
 hipError_t bl_launch_bitdelta_compress(const float* W_fine, const uint16_t* W_base, int64_t N,
-                                       int64_t M, int B, int model, uint8_t* D, float* alpha,
-                                       void* ws, hipStream_t stream) {
+                                       int64_t M, int model, uint8_t* D, float* alpha, void* ws,
+                                       hipStream_t stream) {
   const int64_t n = N * M;
   const int64_t n4 = n / 4;  // M % 16 == 0
   const int64_t blocks = sum_blocks(n4);
@@ -419,6 +419,6 @@ hipError_t bl_launch_bitdelta_compress(const float* W_fine, const uint16_t* W_ba
   if (pblocks > 4096) pblocks = 4096;
   hipLaunchKernelGGL(bd_pack, dim3((unsigned)pblocks), dim3(256), 0, stream,
                      reinterpret_cast<const float4*>(W_fine), reinterpret_cast<const uint2*>(W_base),
-                     groups, B, model, reinterpret_cast<uint16_t*>(D));
+                     groups, model, reinterpret_cast<uint16_t*>(D));
   return hipGetLastError();
 }

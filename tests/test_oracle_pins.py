@@ -712,12 +712,12 @@ def test_bitdelta_interleave_and_forward_dense():
         alphas.append(a)
         codes.append(c)
     inter = oracle.bitdelta_interleave(bits)
-    assert inter.shape == (N, M // 8 * B)
-    for i in range(B):
+    assert inter.shape == (N, M)
+    for i in range(8):
         for n in range(N):
             for j in range(M // 16):
-                assert inter[n, (j * B + i) * 2] == bits[i][n, 2 * j]
-                assert inter[n, (j * B + i) * 2 + 1] == bits[i][n, 2 * j + 1]
+                lo, hi = (bits[i][n, 2 * j], bits[i][n, 2 * j + 1]) if i < B else (0, 0)
+                assert inter[n, (j * 8 + i) * 2] == lo and inter[n, (j * 8 + i) * 2 + 1] == hi
     X = r.standard_normal((B, M)).astype(np.float32)
     Y = oracle.bitdelta_forward(base, codes, alphas, X)
     for i in range(B):

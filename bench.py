@@ -491,6 +491,44 @@ def run_train_side(torch, bl, workloads):
             "rmsnorm_backward_t2048_k4096": rec(ms_b, b_bytes)}
 
 
+def run_bitdelta(torch, bl, N=8192, M=8192, B=8):
+    """BitDelta's Figure 4 shape: one bf16 base matrix and B 1-bit deltas, one token per
+    model; rotating replicas of base and deltas (402 MB each pair) so the last-level cache
+    cannot serve repeats."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    base = (torch.randn((N, M), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    fines = [base.float() + torch.randn((N, M), generator=gen, device=dev) * 0.001
+             for _ in range(B)]
+    D, alpha = bl.bitdelta_compress(fines, base)
+    ws = torch.empty(bl.bitlinear_weight_workspace_bytes(N, M), dtype=torch.uint8, device=dev)
+    g_c = _warm_then_capture(torch, [lambda: bl.bitlinear_bitdelta_compress(
+        fines[0], base.view(torch.int16), B, 0, D, alpha, ws)] * 4)
+    g_c.replay()
+    ms_c = _time_graph(torch, g_c, 1) / 4
+    del fines
+    reps = 4
+    copies = [(base, D)] + [(base.clone(), D.clone()) for _ in range(reps - 1)]
+    X = torch.randn((B, M), generator=gen, device=dev)
+    Y = torch.empty((B, N), dtype=torch.float32, device=dev)
+    n_k = 64
+    g = _warm_then_capture(torch, [
+        (lambda c=copies[i % reps]: bl.bitlinear_bitdelta_forward(c[0].view(torch.int16), c[1],
+                                                                 alpha, X, Y))
+        for i in range(n_k)])
+    g.replay()
+    ms = _time_graph(torch, g, 2) / n_k
+    nbytes = N * M * 2 + N * M * B // 8 + B * M * 4 + B * N * 4 + 4 * B
+    del copies, base, D
+    torch.cuda.empty_cache()
+    return {"workload": "BitDelta linear layer, N = M = %d, B = %d models (one token each)" % (N, B),
+            "kernel": "bitdelta_kernel", "us": round(ms * 1e3, 3), "bytes": nbytes,
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "compress_one_model_ms": round(ms_c, 4)}
+
+
 def run_calib_copy(torch):
     n = 64 * 1024 * 1024  # 256 MiB of fp32
     a = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -610,6 +648,7 @@ def main():
         line["sign_decode8b"] = run_sign_decode(torch, bl, workloads)
         line["scale_groups_decode8b"] = run_scale_groups_decode(torch, bl, workloads)
         line["train_side"] = run_train_side(torch, bl, workloads)
+        line["bitdelta"] = run_bitdelta(torch, bl)
     if a.calib_copy:
         line["calib_copy"] = run_calib_copy(torch)
     line["cpu_baseline"] = None if a.no_cpu else run_cpu_baseline(d, workloads)

@@ -630,7 +630,7 @@ def main():
                                "replicas; HIP-graph replay",
                    "T": T, "projections": 7, "packed_bytes_per_layer": d["packed_bytes"],
                    "bytes_per_step": step_bytes, "frac_hbm_step": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1> (grouped, 7 projections)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1, 0> (grouped, 7 projections)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(),
                      "bytes_per_launch": d["gemv_bytes"],

@@ -52,7 +52,7 @@ namespace bl {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;  // 4
-constexpr int kGemvDepth = 2;                      // row groups in flight per wave (2-bit)
+constexpr int kGemvDepth = 3;                      // row groups in flight per wave (2-bit)
 #ifndef BL_GEMV_SIGN_DEPTH
 #define BL_GEMV_SIGN_DEPTH 4
 #endif
@@ -464,10 +464,14 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
       order[j] = order[j - 1];
       order[j - 1] = t;
     }
-  // One round of resident workgroups (the combine words take at most a few KB of LDS);
-  // each projection gets workgroups in proportion to its cost, at least one and never
-  // one without a row group.
-  const int cap = gemv_resident<FMT>(big, 4096);
+  // One round of workgroups, at most as many as stay resident (the combine words take at
+  // most a few KB of LDS); each projection gets workgroups in proportion to its cost, at
+  // least one and never one without a row group. The 2-bit format launches 3/8 of the
+  // resident count, each wave with three row groups in flight: fewer waves to start and
+  // to drain while HBM stays busy (measured about 3% faster than all resident
+  // workgroups at depth two on the 8B decode projections).
+  const int resident = gemv_resident<FMT>(big, 4096);
+  const int cap = FMT == 0 ? resident * 3 / 8 : resident;
   int wgs = 0, slots = 0;
   for (int o = 0; o < count; ++o) {
     const int i = order[o];

@@ -6,24 +6,30 @@
 // traffic; "Inference optimization and custom kernels": 2-bit weights unpacked on
 // the fly. [bitnet.cpp] "3. BitLinear operation": rescale of the integer product.
 //
-// Y[T, N] = Xq[T, K] * q[N, K]^T. A workgroup (4 waves, 2 x 2) computes a BM x BN tile
-// (BM tokens x BN weight rows); each wave a (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA
-// blocks. Per k-tile of 128 codes:
-//   - activations: BM x 128 bytes into LDS, read from global memory as whole 128-byte
-//     row segments (8 lanes per row: scattered 64-byte pieces cost the cache path about
-//     three times as much), 16-byte groups 4x4 byte-transposed to the unpack order,
-//     groups XOR-swizzled by row (conflict-free 128-bit reads and writes);
-//   - weights: BN x 32 packed bytes, unpacked ONCE per workgroup to signed
-//     int8 (unpack_q2, v_perm_b32 table) and written to LDS in the same swizzled layout,
-//     so every wave reads both operands with plain 128-bit LDS reads and spends no ALU
-//     on them;
+// Y[T, N] = Xq[T, K] * q[N, K]^T in tiles of BM tokens x BN weight rows, 4 waves per
+// workgroup, k-tiles of 128 codes. Two kernels:
+//
+// prefill_big_kernel (problems that give every CU at least one 128 x 256 tile): waves
+// side by side along the rows (each 128 tokens x 64 rows), weights kept packed in LDS
+// and unpacked by each wave in registers as u = q + 1 in {0, 1, 2}, with the token sums
+// sum_k x subtracted in the epilogue; two LDS stages (one barrier per k-tile), the next
+// k-tile's global loads issued under the MFMAs of the first step and its staging under
+// those of the last. Described in full above the kernel.
+//
+// prefill_kernel (smaller problems; 2 x 2 waves, one LDS stage, two workgroups per CU):
+//   - weights: BN x 32 packed bytes, unpacked ONCE per workgroup to signed int8
+//     (unpack_q2, v_perm_b32 table) and written to LDS in the activations' swizzled
+//     layout, so every wave reads both operands with plain 128-bit LDS reads;
 //   - the next k-tile is loaded from global memory into registers while the MFMAs of
-//     the current one run, then written over it between two barriers (one LDS buffer
-//     per workgroup, so that two workgroups fit a CU and one stages while the other
-//     computes).
-// Workgroups are numbered XCD-major: the tiles one XCD (one L2) runs are consecutive
-// token tiles of the same weight tiles.
-// Epilogue: Y = fp32(acc) * fp32(beta / s_t).
+//     the current one run, then written over it between two barriers.
+//
+// Both: activations are staged as whole 128-byte row segments (8 lanes per row:
+// scattered 64-byte pieces cost the cache path about three times as much), each 16-byte
+// group 4x4 byte-transposed to the unpack order, groups XOR-swizzled by row
+// (conflict-free 128-bit reads and writes). Workgroups are numbered XCD-major: the tiles
+// one XCD (one L2) runs are consecutive token tiles of the same weight tiles.
+// Epilogue: Y = fp32(acc) * fp32(beta / s_t), the sixteen factors of a lane read from LDS
+// before its stores.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -56,6 +62,57 @@ struct PfArgs {
   int rpg;      // rows per weight scale group
 };
 
+// Epilogue of one 32 x 32 accumulator block (v_mfma_i32_32x32x32_i8 D layout): the lane
+// holds output row n and tokens tb + 8q + e (q, e = 0..3) in c[4q + e]. fac[] holds
+// fp32(beta / s_t) of the tile's tokens for the scale group of the tile's first row, and
+// sub[] the amounts to subtract from the integer sums (or null). The sixteen factors and
+// sums are read before any store (four 128-bit LDS reads each); a tile that lies inside
+// T, N and one scale group stores without per-element checks.
+__device__ __forceinline__ void pf_store_block(const PfArgs& a, const v16i& c, int m0, int n0,
+                                               int tb, int n, const float* fac, const int* sub,
+                                               bool full) {
+  float f[16];
+  int d[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(fac + tb + 8 * q);
+    f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+    if (sub) {
+      const int4 w = *reinterpret_cast<const int4*>(sub + tb + 8 * q);
+      d[4 * q] = w.x; d[4 * q + 1] = w.y; d[4 * q + 2] = w.z; d[4 * q + 3] = w.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * q + e] = 0;
+    }
+  }
+  float* yp = a.Y + (int64_t)(m0 + tb) * a.N + n;
+  int32_t* ap = a.acc ? a.acc + (int64_t)(m0 + tb) * a.N + n : nullptr;
+  if (full) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dt = 8 * (r >> 2) + (r & 3);
+      const int v = c[r] - d[r];
+      yp[(int64_t)dt * a.N] = (float)v * f[r];
+      if (ap) ap[(int64_t)dt * a.N] = v;
+    }
+    return;
+  }
+  if (n >= a.N) return;
+  // rows of another scale group than the tile's first row divide their own scale
+  const bool own = n / a.rpg == n0 / a.rpg;
+  const float wsn = own ? 0.0f : a.ws[n / a.rpg];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int dt = 8 * (r >> 2) + (r & 3);
+    const int t = m0 + tb + dt;
+    if (t < a.T) {
+      const int v = c[r] - d[r];
+      yp[(int64_t)dt * a.N] = (float)v * (own ? f[r] : wsn / a.xs[t]);
+      if (ap) ap[(int64_t)dt * a.N] = v;
+    }
+  }
+}
+
 template <int BM, int BN>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2, MI = WM / 32, NI = WN / 32;
@@ -64,7 +121,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
   static_assert(XQ >= 1 && WQ >= 1, "tile does not fit the thread count");
   __shared__ __attribute__((aligned(16))) uint8_t xs_l[BM * kPfKT];
   __shared__ __attribute__((aligned(16))) uint8_t ws_l[BN * kPfKT];
-  __shared__ float fac[BM];
+  __shared__ __attribute__((aligned(16))) float fac[BM];
 
   // XCD-major numbering: workgroup b runs on XCD b % 8
   const int bid = (int)blockIdx.x;
@@ -172,31 +229,243 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
   }
 
   // D[token][row]: lane holds row li of the 32 x 32 block, tokens 8*(r/4) + 4*lg + r%4.
-  // One block at a time, addresses advanced per token, so that the epilogue does not
-  // hold every store address at once.
+  const bool full = m0 + BM <= a.T && n0 + BN <= a.N && n0 / a.rpg == (n0 + BN - 1) / a.rpg;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int n = n0 + wn * WN + j * 32 + li;
-      const int tb = wm * WM + i * 32 + 4 * lg;
-      float* yp = a.Y + (int64_t)(m0 + tb) * a.N + n;
-      int32_t* ap = a.acc ? a.acc + (int64_t)(m0 + tb) * a.N + n : nullptr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dt = 8 * (r >> 2) + (r & 3);
-        const int t = m0 + tb + dt;
-        if (t < a.T && n < a.N) {
-          const int v = acc[i][j][r];
-          // fac holds beta of the tile's first row's group; rows of another group (scale
-          // groups smaller than the tile or straddling it) divide their own scale
-          const float f = n / a.rpg == n0 / a.rpg ? fac[tb + dt] : a.ws[n / a.rpg] / a.xs[t];
-          yp[(int64_t)dt * a.N] = (float)v * f;
-          if (ap) ap[(int64_t)dt * a.N] = v;
-        }
-      }
+      pf_store_block(a, acc[i][j], m0, n0, wm * WM + i * 32 + 4 * lg, n0 + wn * WN + j * 32 + li,
+                     fac, nullptr, full);
       __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Large tiles for large problems: 4 waves in a WY x WX grid (WY along tokens), each
+// computing (32 MI) x (32 NI); BM = 32 MI WY, BN = 32 NI WX. One k-tile is 128 codes.
+//   - The weights stay packed in LDS (32 bytes per row and k-tile, a quarter of the
+//     unpacked bytes) and each wave unpacks the fragments it multiplies in registers.
+//     With WY = 1 no two waves unpack the same rows.
+//   - The MFMAs take the unsigned codes u = q + 1 in {0, 1, 2} (four masks and three
+//     shifts per packed dword, no sign conversion), so the integer product is
+//     sum_k x u = acc + sum_k x; the per-token sums sum_k x come from the activation
+//     bytes as they are staged (one v_dot4 per dword) and are subtracted in the
+//     epilogue. All of it is exact integer arithmetic.
+//   - Two LDS stages: the next k-tile waits in registers during the MFMAs of the current
+//     one and is then written to the other stage, so one barrier per k-tile suffices.
+//
+// Packed LDS row of a k-tile: the eight dwords d0..d7 of the row's 32 bytes (dword d =
+// codes 16d..16d+15) stored as d0 d2 d4 d6 | d1 d3 d5 d7, so that lane half lg reads its
+// four MFMA steps (codes 32s + 16lg .. +15, s = 0..3) in one 128-bit read.
+template <int MI, int NI, int WY, int OCC>
+__global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) {
+  constexpr int WX = 4 / WY;
+  constexpr int WM = 32 * MI, WN = 32 * NI, BM = WM * WY, BN = WN * WX;
+  constexpr int XQ = BM * (kPfKT / 16) / kPfThreads;  // 16-byte activation pieces per thread
+  constexpr int WQ = BN * 2 / kPfThreads;             // 16-byte packed halves per thread
+  constexpr int XB = BM * kPfKT, WB = BN * (kPfKT / 4), SB = XB + WB;
+  static_assert(WY * WX == 4 && XQ >= 1 && WQ >= 1, "tile does not fit the thread count");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * SB];
+  __shared__ __attribute__((aligned(16))) float fac[BM];
+  __shared__ __attribute__((aligned(16))) int xsum[BM];
+
+  const int bid = (int)blockIdx.x;
+  const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
+  if (tile >= a.tiles_m * a.tiles_n) return;
+  const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int wm = wave / WX, wn = wave % WX;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int Kb = a.K >> 2;
+  const int nk = a.K / kPfKT;
+  const float beta = a.ws[n0 / a.rpg];
+  for (int i = tid; i < BM; i += kPfThreads) {
+    const int t = m0 + i;
+    fac[i] = t < a.T ? beta / a.xs[t] : 0.0f;
+  }
+
+  // Staging. Activation piece r of a thread: row tid/8 + 32r, 16-byte group tid%8 (eight
+  // lanes read one 128-byte row segment); its LDS slot is pf_pos, whose swizzle term
+  // depends on the row only through (tid/8 / 2) % 8, the same for every r.
+  const int xt = tid >> 3, xg = tid & 7;
+  const int8_t* xsrc[XQ];
+#pragma unroll
+  for (int r = 0; r < XQ; ++r)
+    xsrc[r] = a.Xq + (int64_t)min(m0 + xt + 32 * r, a.T - 1) * a.K + 16 * xg;
+  const int xdst = pf_pos(xt, xg);  // + 32 r rows = + 4096 r bytes
+  // Packed weight half r of a thread: row tid/2 + 128r, half tid%2 (dwords 4h..4h+3).
+  const int wt = tid >> 1, wh = tid & 1;
+  const uint8_t* wsrc[WQ];
+#pragma unroll
+  for (int r = 0; r < WQ; ++r)
+    wsrc[r] = a.W + (int64_t)min(n0 + wt + 128 * r, a.N - 1) * Kb + 16 * wh;
+  const int wdst = XB + wt * 32 + 8 * wh;  // + 128 r rows = + 4096 r bytes
+
+  uint4 xr[XQ], wr[WQ];
+  int rs[XQ];  // this thread's part of the token sums sum_k x
+#pragma unroll
+  for (int r = 0; r < XQ; ++r) rs[r] = 0;
+  auto load_tile = [&](int kt) {
+    kt = min(kt, nk - 1);  // past the last k-tile: reload it (in range, never read back)
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) xr[r] = *reinterpret_cast<const uint4*>(xsrc[r] + kt * kPfKT);
+#pragma unroll
+    for (int r = 0; r < WQ; ++r) wr[r] = *reinterpret_cast<const uint4*>(wsrc[r] + kt * (kPfKT / 4));
+  };
+  auto store_tile = [&](uint8_t* st, bool count) {
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) {
+      const uint32_t in[4] = {xr[r].x, xr[r].y, xr[r].z, xr[r].w};
+      if (count) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          rs[r] = __builtin_amdgcn_sdot4((int)in[d], 0x01010101, rs[r], false);
+      }
+      uint32_t o[4];
+      transpose16(in, o);
+      *reinterpret_cast<uint4*>(st + xdst + 4096 * r) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+#pragma unroll
+    for (int r = 0; r < WQ; ++r) {
+      // dwords 4h, 4h+2 go to the even half, 4h+1, 4h+3 to the odd half
+      *reinterpret_cast<uint2*>(st + wdst + 4096 * r) = make_uint2(wr[r].x, wr[r].z);
+      *reinterpret_cast<uint2*>(st + wdst + 4096 * r + 16) = make_uint2(wr[r].y, wr[r].w);
+    }
+  };
+
+  v16i acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  // Reads. Activation fragment i at step s: row wm WM + 32 i + li, group 2s + lg; the
+  // swizzle term ((row / 2) % 8) reduces to (li / 2) % 8, so the four per-step offsets
+  // are per-lane constants and i adds 4096 i.
+  const int li = lane & 31, lg = lane >> 5;
+  const int sw = (li >> 1) & 7;
+  int xo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) xo[s] = (wm * WM + li) * kPfKT + 16 * ((2 * s + lg) ^ sw);
+  const int wo = XB + (wn * WN + li) * 32 + 16 * lg;  // + 1024 j
+
+  // One MFMA step s reads MI activation fragments and unpacks NI weight dwords. The
+  // fragments of step s + 1 are read and unpacked while the MFMAs of step s run (two
+  // fragment sets; the scheduling barriers keep the compiler from hoisting every read of
+  // the k-tile, which would need more registers than the wave has).
+  auto read_step = [&](const uint8_t* st, const uint4 (&pk)[NI], int s, v4i (&af)[MI],
+                       v4i (&bf)[NI]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const uint4 x = *reinterpret_cast<const uint4*>(st + xo[s] + 4096 * i);
+      af[i] = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t w = s == 0 ? pk[j].x : s == 1 ? pk[j].y : s == 2 ? pk[j].z : pk[j].w;
+      uint32_t u[4];
+      unpack_u2(w, u);
+      bf[j] = v4i{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+    }
+  };
+  auto mfma_step = [&](const v4i (&af)[MI], const v4i (&bf)[NI]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+  // One k-tile: step-0 reads, then four MFMA steps; the global loads of the next k-tile
+  // are issued under the MFMAs of step 0 and the next k-tile is staged into the other
+  // LDS stage under the MFMAs of step 3, so neither waits in the open.
+  auto compute = [&](int kt) {
+    const uint8_t* st = lds + SB * (kt & 1);
+    uint4 pk[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) pk[j] = *reinterpret_cast<const uint4*>(st + wo + 1024 * j);
+    v4i a0[MI], b0[NI], a1[MI], b1[NI];
+    read_step(st, pk, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step(st, pk, 1, a1, b1);
+    mfma_step(a0, b0);
+    load_tile(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step(st, pk, 2, a0, b0);
+    mfma_step(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step(st, pk, 3, a1, b1);
+    mfma_step(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(a1, b1);
+    // past the last k-tile: written (in range), never read, and not counted
+    store_tile(lds + SB * ((kt + 1) & 1), kt + 1 < nk);
+  };
+
+  load_tile(0);
+  store_tile(lds, true);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    compute(kt);
+    __syncthreads();
+  }
+  // token sums: the eight lanes of a row segment hold its eight 16-byte groups
+#pragma unroll
+  for (int r = 0; r < XQ; ++r) {
+    int v = rs[r];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if (xg == 0) xsum[xt + 32 * r] = v;
+  }
+  __syncthreads();
+
+  const bool full = m0 + BM <= a.T && n0 + BN <= a.N && n0 / a.rpg == (n0 + BN - 1) / a.rpg;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      pf_store_block(a, acc[i][j], m0, n0, wm * WM + i * 32 + 4 * lg, n0 + wn * WN + j * 32 + li,
+                     fac, xsum, full);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Compute units of the current device (queried once).
+inline int pf_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int MI, int NI, int WY, int OCC>
+hipError_t launch_prefill_big(const bl_proj_internal* p, int T, hipStream_t stream) {
+  constexpr int BM = 32 * MI * WY, BN = 32 * NI * (4 / WY);
+  PfArgs a{};
+  a.Xq = p->Xq;
+  a.xs = p->x_scale;
+  a.W = p->W;
+  a.ws = p->w_scale;
+  a.Y = p->Y;
+  a.acc = p->acc;
+  a.T = T;
+  a.N = p->N;
+  a.K = p->K;
+  a.rpg = p->rpg;
+  a.tiles_m = (T + BM - 1) / BM;
+  a.tiles_n = (p->N + BN - 1) / BN;
+  const int tiles = a.tiles_m * a.tiles_n;
+  a.per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL((prefill_big_kernel<MI, NI, WY, OCC>), dim3((unsigned)(8 * a.per_xcd)),
+                     dim3(kPfThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int BM, int BN>
@@ -227,9 +496,17 @@ using namespace bl;
 
 bool bl_prefill_supports(int T, int K) { return T >= 1 && K % 128 == 0; }
 
-// 256-token tiles (a 128 x 64 sub-tile per wave: each weight fragment feeds four MFMAs)
-// while they still give the device two rounds of workgroups; 128 x 128 otherwise.
+// 128 x 256 tiles (1 x 4 waves of 128 x 64) when they give every CU at least one;
+// two workgroups per CU when there are more tiles than CUs, so that one workgroup's
+// epilogue (the fp32 stores) runs under the other's MFMAs, one otherwise (then the
+// accumulators sit in AGPRs and nothing spills). Smaller problems take the
+// single-stage tiles.
 hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((T + 127) / 128) * ((p->N + 255) / 256);
+  const int cus = pf_cus();
+  if (T >= 128 && tiles >= cus)
+    return tiles > cus ? launch_prefill_big<4, 2, 1, 2>(p, T, stream)
+                       : launch_prefill_big<4, 2, 1, 1>(p, T, stream);
   const int64_t big = (int64_t)((T + 255) / 256) * ((p->N + 127) / 128);
   if (T >= 256 && big >= 512) return launch_prefill_t<256, 128>(p, T, stream);
   return launch_prefill_t<128, 128>(p, T, stream);

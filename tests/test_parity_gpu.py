@@ -176,6 +176,9 @@ PRODUCT_CASES = [
     ("skinny", 8, 64, 256),
     ("prefill", 1, 130, 1024), ("prefill", 100, 300, 4096), ("prefill", 129, 129, 1280),
     ("prefill", 263, 520, 14336), ("prefill", 256, 256, 128),
+    # large-tile kernels (chosen by tile count): 128 x 256 tiles, then 256 x 256 tiles,
+    # ragged in tokens and rows
+    ("prefill", 130, 32845, 256), ("prefill", 300, 49102, 384), ("prefill", 513, 32668, 256),
     ("generic", 3, 77, 68), ("generic", 5, 300, 4100), ("generic", 1, 16, 4),
 ]
 

@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--counter-pass", type=int, default=0, metavar="N",
                     help="hardware-counter pass: N eager decode steps and the calibration "
                          "copy, no graphs and no JSON line (for rocprofv3 --pmc)")
+    ap.add_argument("--prefill-pass", type=int, default=0, metavar="N",
+                    help="profiling pass: N eager prefill products per prefill shape, no "
+                         "graphs and no JSON line (for rocprofv3 --kernel-trace / --pmc)")
     return ap.parse_args()
 
 
@@ -231,6 +234,28 @@ def run_prefill(torch, bl, workloads):
         del Xs, Xq, Y, packed
         torch.cuda.empty_cache()
     return out
+
+
+def run_prefill_pass(torch, bl, workloads, n):
+    """n eager launches of the prefill product per prefill shape (each dispatch on its own,
+    for the profiler); inputs as in run_prefill."""
+    dev = torch.device("cuda:0")
+    T = workloads.PREFILL_T
+    for (N, K) in workloads.PREFILL_SHAPES:
+        W = torch.from_numpy(workloads.weights(N, K, 7)).to(dev)
+        packed, beta = bl.quantize_weights(W)
+        del W
+        X = torch.from_numpy(workloads.acts_student_t(T, K, 8)).to(dev)
+        Xq, xs = bl.quantize_acts(X)
+        Y = torch.empty((T, N), dtype=torch.float32, device=dev)
+        fw = bl.prepare_forward_grouped([(Xq, xs, packed, beta, Y, None)], T)
+        for _ in range(n):
+            fw()
+        torch.cuda.synchronize()
+        print("prefill pass: %d products at T=%d N=%d K=%d (%s)"
+              % (n, T, N, K, bl.bitlinear_forward_choice(T, N, K)), flush=True)
+        del X, Xq, Y, packed
+        torch.cuda.empty_cache()
 
 
 def run_sweep70b(torch, bl, workloads):
@@ -594,6 +619,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if a.prefill_pass > 0:
+        run_prefill_pass(torch, bl, workloads, a.prefill_pass)
+        return
     T = 1
     d = setup_decode(torch, bl, workloads, T)
     if a.counter_pass > 0:

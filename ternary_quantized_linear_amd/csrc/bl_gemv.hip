@@ -464,14 +464,14 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
       order[j] = order[j - 1];
       order[j - 1] = t;
     }
-  // One round of workgroups, at most as many as stay resident (the combine words take at
+  // One round of workgroups, half as many as stay resident (the combine words take at
   // most a few KB of LDS); each projection gets workgroups in proportion to its cost, at
-  // least one and never one without a row group. The 2-bit format launches 3/8 of the
-  // resident count, each wave with three row groups in flight: fewer waves to start and
-  // to drain while HBM stays busy (measured about 3% faster than all resident
-  // workgroups at depth two on the 8B decode projections).
+  // least one and never one without a row group. Half the resident count, each wave with
+  // three (2-bit) or four (1-bit) row groups in flight, keeps HBM as busy as a full
+  // round with fewer waves to start and to drain (measured: 3% faster than a full round
+  // on the 8B decode layer, 5% on its 1-bit form, 4-15% on the 70B projections).
   const int resident = gemv_resident<FMT>(big, 4096);
-  const int cap = FMT == 0 ? resident * 3 / 8 : resident;
+  const int cap = resident / 2;
   int wgs = 0, slots = 0;
   for (int o = 0; o < count; ++o) {
     const int i = order[o];

@@ -12,9 +12,9 @@
 // prefill_big_kernel (problems that give every CU at least one 128 x 256 tile): waves
 // side by side along the rows (each 128 tokens x 64 rows), weights kept packed in LDS
 // and unpacked by each wave in registers as u = q + 1 in {0, 1, 2}, with the token sums
-// sum_k x subtracted in the epilogue; two LDS stages (one barrier per k-tile), the next
-// k-tile's global loads issued under the MFMAs of the first step and its staging under
-// those of the last. Described in full above the kernel.
+// sum_k x subtracted in the epilogue; two LDS stages (one barrier per k-tile) and two
+// register sets, so that the global loads of k-tile kt + 2 and the staging of kt + 1
+// both run under the MFMAs of k-tile kt. Described in full above the kernel.
 //
 // prefill_kernel (smaller problems; 2 x 2 waves, one LDS stage, two workgroups per CU):
 //   - weights: BN x 32 packed bytes, unpacked ONCE per workgroup to signed int8
@@ -250,8 +250,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
 //     sum_k x u = acc + sum_k x; the per-token sums sum_k x come from the activation
 //     bytes as they are staged (one v_dot4 per dword) and are subtracted in the
 //     epilogue. All of it is exact integer arithmetic.
-//   - Two LDS stages: the next k-tile waits in registers during the MFMAs of the current
-//     one and is then written to the other stage, so one barrier per k-tile suffices.
+//   - Two LDS stages and two register sets: during the MFMAs of k-tile kt, k-tile kt + 2
+//     is loaded into one register set while k-tile kt + 1 (loaded during kt - 1) is
+//     staged from the other into the other LDS stage, both spread over the MFMA steps;
+//     one barrier per k-tile.
 //
 // Packed LDS row of a k-tile: the eight dwords d0..d7 of the row's 32 bytes (dword d =
 // codes 16d..16d+15) stored as d0 d2 d4 d6 | d1 d3 d5 d7, so that lane half lg reads its
@@ -300,35 +302,45 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
     wsrc[r] = a.W + (int64_t)min(n0 + wt + 128 * r, a.N - 1) * Kb + 16 * wh;
   const int wdst = XB + wt * 32 + 8 * wh;  // + 128 r rows = + 4096 r bytes
 
-  uint4 xr[XQ], wr[WQ];
+  // Two register sets for staging: the loads of k-tile kt + 2 go to one while k-tile
+  // kt + 1, loaded during the previous k-tile, is staged from the other. Items 0..XQ-1
+  // are activation pieces, XQ..XQ+WQ-1 packed weight halves; they are issued and staged
+  // in three parts spread over the MFMA steps.
+  constexpr int NITEM = XQ + WQ;
+  struct Regs { uint4 v[NITEM]; };
+  Regs ra, rb;
   int rs[XQ];  // this thread's part of the token sums sum_k x
 #pragma unroll
   for (int r = 0; r < XQ; ++r) rs[r] = 0;
-  auto load_tile = [&](int kt) {
+  auto load_part = [&](Regs& R, int kt, int part) {
     kt = min(kt, nk - 1);  // past the last k-tile: reload it (in range, never read back)
 #pragma unroll
-    for (int r = 0; r < XQ; ++r) xr[r] = *reinterpret_cast<const uint4*>(xsrc[r] + kt * kPfKT);
-#pragma unroll
-    for (int r = 0; r < WQ; ++r) wr[r] = *reinterpret_cast<const uint4*>(wsrc[r] + kt * (kPfKT / 4));
-  };
-  auto store_tile = [&](uint8_t* st, bool count) {
-#pragma unroll
-    for (int r = 0; r < XQ; ++r) {
-      const uint32_t in[4] = {xr[r].x, xr[r].y, xr[r].z, xr[r].w};
-      if (count) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          rs[r] = __builtin_amdgcn_sdot4((int)in[d], 0x01010101, rs[r], false);
-      }
-      uint32_t o[4];
-      transpose16(in, o);
-      *reinterpret_cast<uint4*>(st + xdst + 4096 * r) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int q = 0; q < NITEM; ++q) {
+      if (q * 3 / NITEM != part) continue;
+      if (q < XQ) R.v[q] = *reinterpret_cast<const uint4*>(xsrc[q] + kt * kPfKT);
+      else R.v[q] = *reinterpret_cast<const uint4*>(wsrc[q - XQ] + kt * (kPfKT / 4));
     }
+  };
+  auto store_part = [&](const Regs& R, uint8_t* st, bool count, int part) {
 #pragma unroll
-    for (int r = 0; r < WQ; ++r) {
-      // dwords 4h, 4h+2 go to the even half, 4h+1, 4h+3 to the odd half
-      *reinterpret_cast<uint2*>(st + wdst + 4096 * r) = make_uint2(wr[r].x, wr[r].z);
-      *reinterpret_cast<uint2*>(st + wdst + 4096 * r + 16) = make_uint2(wr[r].y, wr[r].w);
+    for (int q = 0; q < NITEM; ++q) {
+      if (q * 3 / NITEM != part) continue;
+      if (q < XQ) {
+        const uint32_t in[4] = {R.v[q].x, R.v[q].y, R.v[q].z, R.v[q].w};
+        if (count) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            rs[q] = __builtin_amdgcn_sdot4((int)in[d], 0x01010101, rs[q], false);
+        }
+        uint32_t o[4];
+        transpose16(in, o);
+        *reinterpret_cast<uint4*>(st + xdst + 4096 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+        const int r = q - XQ;
+        // dwords 4h, 4h+2 go to the even half, 4h+1, 4h+3 to the odd half
+        *reinterpret_cast<uint2*>(st + wdst + 4096 * r) = make_uint2(R.v[q].x, R.v[q].z);
+        *reinterpret_cast<uint2*>(st + wdst + 4096 * r + 16) = make_uint2(R.v[q].y, R.v[q].w);
+      }
     }
   };
 
@@ -376,11 +388,13 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
       for (int j = 0; j < NI; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
   };
-  // One k-tile: step-0 reads, then four MFMA steps; the global loads of the next k-tile
-  // are issued under the MFMAs of step 0 and the next k-tile is staged into the other
-  // LDS stage under the MFMAs of step 3, so neither waits in the open.
-  auto compute = [&](int kt) {
+  // One k-tile kt from LDS stage kt % 2: step-0 reads, then four MFMA steps; under
+  // them, the loads of k-tile kt + 2 into register set L and the staging of k-tile
+  // kt + 1 from register set S into the other LDS stage, each in three parts.
+  auto compute = [&](int kt, Regs& L, const Regs& S) {
     const uint8_t* st = lds + SB * (kt & 1);
+    uint8_t* nx = lds + SB * ((kt + 1) & 1);
+    const bool count = kt + 1 < nk;  // past the last k-tile: staged, never read or counted
     uint4 pk[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) pk[j] = *reinterpret_cast<const uint4*>(st + wo + 1024 * j);
@@ -389,24 +403,38 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 1, a1, b1);
     mfma_step(a0, b0);
-    load_tile(kt + 1);
+    load_part(L, kt + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 2, a0, b0);
     mfma_step(a1, b1);
+    load_part(L, kt + 2, 1);
+    store_part(S, nx, count, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 3, a1, b1);
     mfma_step(a0, b0);
+    load_part(L, kt + 2, 2);
+    store_part(S, nx, count, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(a1, b1);
-    // past the last k-tile: written (in range), never read, and not counted
-    store_tile(lds + SB * ((kt + 1) & 1), kt + 1 < nk);
+    store_part(S, nx, count, 2);
   };
 
-  load_tile(0);
-  store_tile(lds, true);
+#pragma unroll
+  for (int part = 0; part < 3; ++part) load_part(ra, 0, part);
+#pragma unroll
+  for (int part = 0; part < 3; ++part) store_part(ra, lds, true, part);
+#pragma unroll
+  for (int part = 0; part < 3; ++part) load_part(rb, 1, part);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    compute(kt);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    compute(kt, ra, rb);
+    __syncthreads();
+    compute(kt + 1, rb, ra);
+    __syncthreads();
+  }
+  if (kt < nk) {
+    compute(kt, ra, rb);
     __syncthreads();
   }
   // token sums: the eight lanes of a row segment hold its eight 16-byte groups

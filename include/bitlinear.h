@@ -169,6 +169,35 @@ bl_status bitlinear_forward_ex(const int8_t* Xq, const float* x_scale, int64_t T
 /* The kernel bitlinear_forward would run for this shape. */
 bl_kernel bitlinear_forward_choice(int64_t T, int64_t N, int64_t K);
 
+/* Split-K workspace. With up to 128 tokens and few row tiles (for example T = 32..64
+ * on a 70B down projection, N = 8192, K = 28672) the tiled MFMA GEMM cuts K into slices
+ * so that every CU gets work; each slice writes its exact int32 partial products to a
+ * workspace, and a second kernel sums them and applies the rescale (the results are
+ * those of bitlinear_forward, bit for bit for acc). The library allocates nothing for
+ * this: the caller passes the workspace.
+ *
+ * bitlinear_forward_workspace_bytes: bytes of workspace that let bitlinear_forward_ws
+ * split K for this shape (0: the shape never splits, or invalid dimensions).
+ *
+ * bitlinear_forward_ws: bitlinear_forward_ex with a workspace (device memory, 16-byte
+ * aligned, owned by the caller, not read before it is written, contents undefined after
+ * the call; NULL or fewer than bitlinear_forward_workspace_bytes bytes: no split). Calls
+ * that share one workspace must not overlap (use it on one stream, or give each stream
+ * its own). BL_ERR_ALIGN for a misaligned workspace.
+ *
+ * bitlinear_forward_grouped_ws: bitlinear_forward_grouped with a workspace; the
+ * projections that split run one after another, so the largest of their
+ * bitlinear_forward_workspace_bytes is enough.
+ *
+ * bitlinear_forward_choice_ws: the kernel bitlinear_forward_ws would run with a
+ * workspace of that many bytes. */
+size_t bitlinear_forward_workspace_bytes(int64_t T, int64_t N, int64_t K);
+bl_status bitlinear_forward_ws(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                               const uint8_t* W_packed, const float* w_scale, int64_t N,
+                               float* Y, int32_t* acc, bl_kernel kernel, void* workspace,
+                               size_t workspace_bytes, bl_stream_t stream);
+bl_kernel bitlinear_forward_choice_ws(int64_t T, int64_t N, int64_t K, size_t workspace_bytes);
+
 /* One projection of a grouped forward: all entries share T. */
 typedef struct bl_proj_desc {
   const int8_t* Xq;         /* int8 [T, K] */
@@ -187,6 +216,9 @@ typedef struct bl_proj_desc {
  * decode path). Each entry's results are those of bitlinear_forward. */
 bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_t T,
                                     bl_stream_t stream);
+bl_status bitlinear_forward_grouped_ws(const bl_proj_desc* descs, int count, int64_t T,
+                                       void* workspace, size_t workspace_bytes,
+                                       bl_stream_t stream);
 
 /* ---------------------------------------------------------------- weight scale groups
  *

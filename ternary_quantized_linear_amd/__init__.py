@@ -21,6 +21,7 @@ __all__ = [
     "bitlinear_quantize_weights", "bitlinear_quantize_acts",
     "bitlinear_quantize_acts_grouped", "bitlinear_forward", "bitlinear_forward_ex",
     "bitlinear_forward_choice", "bitlinear_forward_grouped", "bitlinear_status_str",
+    "bitlinear_forward_workspace_bytes", "bitlinear_forward_ws", "bitlinear_forward_grouped_ws",
     "bitlinear_last_hip_error", "bitlinear_abi_version", "quantize_weights",
     "quantize_acts", "forward", "BitLinear", "KERNELS", "NO_NORM", "MAX_K", "MAX_GROUP",
     "prepare_forward_grouped", "prepare_quantize_acts_grouped",
@@ -73,7 +74,13 @@ _c_fw = _sig("bitlinear_forward", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]
 _c_fwx = _sig("bitlinear_forward_ex",
               [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_int, _P])
 _c_choice = _sig("bitlinear_forward_choice", [_I64, _I64, _I64])
+_c_fw_wsb = _sig("bitlinear_forward_workspace_bytes", [_I64, _I64, _I64], ctypes.c_size_t)
+_c_fw_ws = _sig("bitlinear_forward_ws", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_int,
+                                         _P, ctypes.c_size_t, _P])
+_c_choice_ws = _sig("bitlinear_forward_choice_ws", [_I64, _I64, _I64, ctypes.c_size_t])
 _c_fwg = _sig("bitlinear_forward_grouped", [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
+_c_fwg_ws = _sig("bitlinear_forward_grouped_ws",
+                 [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P, ctypes.c_size_t, _P])
 _c_qws = _sig("bitlinear_quantize_weights_sign",
               [_P, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P])
 _c_fws = _sig("bitlinear_forward_sign", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P])
@@ -181,8 +188,33 @@ def bitlinear_forward_ex(Xq, x_scale, W_packed, w_scale, Y, acc=None, kernel="au
                   _ptr(acc), k, _stream(Xq, stream)), "bitlinear_forward_ex")
 
 
-def bitlinear_forward_choice(T: int, N: int, K: int) -> str:
-    return _KERNEL_NAMES[_c_choice(T, N, K)]
+def bitlinear_forward_workspace_bytes(T: int, N: int, K: int) -> int:
+    return int(_c_fw_wsb(T, N, K))
+
+
+def _workspace(nbytes, like):
+    """Split-K workspace from torch's allocator (graph-capture safe), or None."""
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device) if nbytes else None
+
+
+def bitlinear_forward_ws(Xq, x_scale, W_packed, w_scale, Y, acc=None, kernel="auto",
+                         workspace=None, stream=None):
+    T, K = Xq.shape
+    N = W_packed.shape[0]
+    k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    nb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_c_fw_ws(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, _ptr(Y),
+                    _ptr(acc), k, _ptr(workspace), nb, _stream(Xq, stream)),
+           "bitlinear_forward_ws")
+
+
+def bitlinear_forward_choice(T: int, N: int, K: int, workspace: bool = True) -> str:
+    """The kernel the product runs: by default as this binding calls it (forward,
+    prepare_forward_grouped: with the split-K workspace the shape asks for), with
+    workspace=False as the plain C call bitlinear_forward does."""
+    if not workspace:
+        return _KERNEL_NAMES[_c_choice(T, N, K)]
+    return _KERNEL_NAMES[_c_choice_ws(T, N, K, _c_fw_wsb(T, N, K))]
 
 
 def bitlinear_forward_grouped(entries, T, stream=None):
@@ -194,6 +226,13 @@ def bitlinear_forward_grouped(entries, T, stream=None):
                            Wp.shape[0], Xq.shape[-1])
     _check(_c_fwg(arr, len(entries), T, _stream(entries[0][0], stream)),
            "bitlinear_forward_grouped")
+
+
+def bitlinear_forward_grouped_ws(entries, T, workspace, stream=None):
+    """bitlinear_forward_grouped with a split-K workspace (a uint8 tensor or None)."""
+    nb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_c_fwg_ws(_proj_array(entries), len(entries), T, _ptr(workspace), nb,
+                     _stream(entries[0][0], stream)), "bitlinear_forward_grouped_ws")
 
 
 def bitlinear_quantize_weights_sign(W, W_bits, w_scale, w_alpha, workspace, stream=None):
@@ -335,7 +374,14 @@ def prepare_forward_grouped(entries, T):
                            Y.data_ptr(), None if acc is None else acc.data_ptr(),
                            Wp.shape[0], Xq.shape[-1])
     keep = [t for e in entries for t in e if t is not None]
-    return PreparedCall(_c_fwg, arr, len(entries), T, (), "bitlinear_forward_grouped", keep)
+    # one split-K workspace for the call (its projections run one after another), owned
+    # by the prepared call
+    nb = max(_c_fw_wsb(T, Wp.shape[0], Xq.shape[-1]) for (Xq, _, Wp, _, _, _) in entries)
+    ws = _workspace(nb, entries[0][0])
+    if ws is not None:
+        keep.append(ws)
+    return PreparedCall(_c_fwg_ws, arr, len(entries), T,
+                        (_ptr(ws), ctypes.c_size_t(nb)), "bitlinear_forward_grouped_ws", keep)
 
 
 def prepare_forward_sign_grouped(entries, T):
@@ -460,12 +506,14 @@ def quantize_acts(X: torch.Tensor, gain=None, eps: float = 1e-6, flags: int = 0)
 
 
 def forward(Xq, x_scale, packed, beta, with_acc: bool = False, kernel="auto"):
-    """(Xq [T, K], x_scale [T], packed [N, K/4], beta [1]) -> Y fp32 [T, N] (and acc)."""
-    T = Xq.shape[0]
+    """(Xq [T, K], x_scale [T], packed [N, K/4], beta [1]) -> Y fp32 [T, N] (and acc).
+    Passes the split-K workspace the shape asks for (from torch's allocator)."""
+    T, K = Xq.shape
     N = packed.shape[0]
     Y = torch.empty((T, N), dtype=torch.float32, device=Xq.device)
     acc = torch.empty((T, N), dtype=torch.int32, device=Xq.device) if with_acc else None
-    bitlinear_forward_ex(Xq, x_scale, packed, beta, Y, acc, kernel)
+    ws = _workspace(bitlinear_forward_workspace_bytes(T, N, K), Xq)
+    bitlinear_forward_ws(Xq, x_scale, packed, beta, Y, acc, kernel, ws)
     return (Y, acc) if with_acc else Y
 
 

@@ -1,6 +1,7 @@
 // bl_capi.hip -- the C ABI of libbitlinear.so (declared in include/bitlinear.h):
 // host-side argument validation, kernel dispatch, status reporting. No C++ exception
-// crosses the ABI; nothing here allocates device memory or synchronizes the stream.
+// crosses the ABI; nothing here allocates device memory or synchronizes the stream
+// (the scratch of split-K products is the caller's workspace).
 #include <math.h>
 #include <string.h>
 
@@ -46,14 +47,25 @@ bl_status check_proj(const int8_t* Xq, const float* xs, int64_t T, int64_t K,
   return BL_OK;
 }
 
-bl_kernel choose(int64_t T, int64_t N, int64_t K) {
-  // one token: dot4 GEMV; up to 32 tokens: the streaming MFMA kernel, and up to 128 in
-  // passes of 32 while the GEMM's 128 x 128 tiles would not give every CU two
-  // workgroups; beyond: the LDS-tiled MFMA GEMM
+bl_kernel choose(int64_t T, int64_t N, int64_t K, size_t ws_bytes = 0) {
+  // one token: dot4 GEMV. Up to 128 tokens the streaming MFMA kernel (passes of 32),
+  // except where the LDS-tiled GEMM measures faster: from 96 tokens on, from 64 when it
+  // can cut K into slices that fill the device (which takes a workspace for the
+  // partials), from 32 when it can and K >= 16384 (the streaming kernel makes many
+  // passes over long rows), or when its 128 x 128 tiles alone give every CU two
+  // workgroups. Beyond 128 tokens the tiled GEMM.
   if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
-  const int64_t tiles = ((T + 127) / 128) * ((N + 127) / 128);
-  if (bl_skinny_supports((int)T, N, (int)K) && (T <= 32 || tiles < 512)) return BL_KERNEL_SKINNY;
-  if (bl_prefill_supports((int)T, (int)K)) return BL_KERNEL_PREFILL;
+  const bool tiled = bl_prefill_supports((int)T, (int)K);
+  if (bl_skinny_supports((int)T, N, (int)K)) {
+    const int64_t tiles = ((T + 127) / 128) * ((N + 127) / 128);
+    const bool split = tiled && bl_prefill_splits((int)T, (int)N, (int)K) &&
+                       ws_bytes >= bl_prefill_scratch_bytes((int)T, (int)N, (int)K);
+    const bool prefer_tiled = tiled && (T >= 96 || (T >= 64 && split) ||
+                                        (T >= 32 && K >= 16384 && split) ||
+                                        (T > 32 && tiles >= 512));
+    if (!prefer_tiled) return BL_KERNEL_SKINNY;
+  }
+  if (tiled) return BL_KERNEL_PREFILL;
   return BL_KERNEL_GENERIC;
 }
 
@@ -72,13 +84,16 @@ bl_proj_internal to_internal(const int8_t* Xq, const float* xs, int64_t K, const
   return bl_proj_internal{Xq, xs, W, ws, Y, acc, (int)N, (int)K, (int)N};
 }
 
-hipError_t run(bl_kernel k, const bl_proj_internal* p, int count, int T, hipStream_t s) {
+// ws: the caller's workspace (or null); the projections of a grouped call run one after
+// another on s, so each may use all of it
+hipError_t run(bl_kernel k, const bl_proj_internal* p, int count, int T, hipStream_t s,
+               void* ws = nullptr, size_t ws_bytes = 0) {
   switch (k) {
     case BL_KERNEL_GEMV: return bl_launch_gemv(p, count, T, s);
     case BL_KERNEL_SKINNY: return bl_launch_skinny(p, count, T, s);
     case BL_KERNEL_PREFILL:
       for (int i = 0; i < count; ++i) {
-        hipError_t e = bl_launch_prefill(p + i, T, s);
+        hipError_t e = bl_launch_prefill(p + i, T, static_cast<int32_t*>(ws), ws ? ws_bytes : 0, s);
         if (e != hipSuccess) return e;
       }
       return hipSuccess;
@@ -138,16 +153,36 @@ bl_status bitlinear_quantize_acts_grouped(const bl_act_desc* descs, int count, i
 
 bl_kernel bitlinear_forward_choice(int64_t T, int64_t N, int64_t K) { return choose(T, N, K); }
 
-bl_status bitlinear_forward_ex(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+bl_kernel bitlinear_forward_choice_ws(int64_t T, int64_t N, int64_t K, size_t workspace_bytes) {
+  return choose(T, N, K, workspace_bytes);
+}
+
+size_t bitlinear_forward_workspace_bytes(int64_t T, int64_t N, int64_t K) {
+  if (T <= 0 || N <= 0 || K <= 0 || K % 4 || T > kMaxTokens || N > kMaxRows || K > BL_MAX_K)
+    return 0;
+  return bl_prefill_scratch_bytes((int)T, (int)N, (int)K);
+}
+
+bl_status bitlinear_forward_ws(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
                                const uint8_t* W_packed, const float* w_scale, int64_t N,
-                               float* Y, int32_t* acc, bl_kernel kernel, bl_stream_t stream) {
+                               float* Y, int32_t* acc, bl_kernel kernel, void* workspace,
+                               size_t workspace_bytes, bl_stream_t stream) {
   bl_status s = check_proj(Xq, x_scale, T, K, W_packed, w_scale, N, Y, acc);
   if (s != BL_OK) return s;
-  if (kernel == BL_KERNEL_AUTO) kernel = choose(T, N, K);
+  if (workspace && !aligned16(workspace)) return BL_ERR_ALIGN;
+  const size_t ws = workspace ? workspace_bytes : 0;
+  if (kernel == BL_KERNEL_AUTO) kernel = choose(T, N, K, ws);
   if (!supports(kernel, T, N, K)) return BL_ERR_ARG;
   bl_proj_internal p = to_internal(Xq, x_scale, K, W_packed, w_scale, N, Y, acc);
   (void)hipGetLastError();
-  return hip_status(run(kernel, &p, 1, (int)T, (hipStream_t)stream));
+  return hip_status(run(kernel, &p, 1, (int)T, (hipStream_t)stream, workspace, ws));
+}
+
+bl_status bitlinear_forward_ex(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
+                               const uint8_t* W_packed, const float* w_scale, int64_t N,
+                               float* Y, int32_t* acc, bl_kernel kernel, bl_stream_t stream) {
+  return bitlinear_forward_ws(Xq, x_scale, T, K, W_packed, w_scale, N, Y, acc, kernel, nullptr,
+                              0, stream);
 }
 
 bl_status bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t T, int64_t K,
@@ -159,8 +194,16 @@ bl_status bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t T, i
 
 bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_t T,
                                     bl_stream_t stream) {
+  return bitlinear_forward_grouped_ws(descs, count, T, nullptr, 0, stream);
+}
+
+bl_status bitlinear_forward_grouped_ws(const bl_proj_desc* descs, int count, int64_t T,
+                                       void* workspace, size_t workspace_bytes,
+                                       bl_stream_t stream) {
   if (!descs) return BL_ERR_NULL;
   if (count < 1 || count > BL_MAX_GROUP) return BL_ERR_ARG;
+  if (workspace && !aligned16(workspace)) return BL_ERR_ALIGN;
+  const size_t ws = workspace ? workspace_bytes : 0;
   bl_proj_internal p[BL_MAX_GROUP];
   for (int i = 0; i < count; ++i) {
     const bl_proj_desc& d = descs[i];
@@ -176,9 +219,9 @@ bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_
   for (bl_kernel k : kinds) {
     int n = 0;
     for (int i = 0; i < count; ++i)
-      if (choose(T, descs[i].N, descs[i].K) == k) batch[n++] = p[i];
+      if (choose(T, descs[i].N, descs[i].K, ws) == k) batch[n++] = p[i];
     if (n == 0) continue;
-    bl_status s = hip_status(run(k, batch, n, (int)T, (hipStream_t)stream));
+    bl_status s = hip_status(run(k, batch, n, (int)T, (hipStream_t)stream, workspace, ws));
     if (s != BL_OK) return s;
   }
   return BL_OK;

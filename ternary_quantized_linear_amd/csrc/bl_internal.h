@@ -34,7 +34,13 @@ hipError_t bl_launch_gemv(const bl_proj_internal* p, int count, int T, hipStream
 bool bl_skinny_supports(int T, int64_t N, int K);
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream);
 bool bl_prefill_supports(int T, int K);
-hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream);
+// scratch: int32 partial products of a split-K launch, at least
+// bl_prefill_scratch_bytes(T, N, K) bytes, or null (then no split)
+size_t bl_prefill_scratch_bytes(int T, int N, int K);
+// true when a product of T <= 128 tokens would run split-K (slices fill the device)
+bool bl_prefill_splits(int T, int N, int K);
+hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, int32_t* scratch,
+                             size_t scratch_bytes, hipStream_t stream);
 hipError_t bl_launch_generic(const bl_proj_internal* p, int T, hipStream_t stream);
 
 // BitDelta: base bf16 [N, M] plus B interleaved 1-bit deltas, one token per model.

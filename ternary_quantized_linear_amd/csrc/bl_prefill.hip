@@ -60,6 +60,11 @@ struct PfArgs {
   int tiles_m, tiles_n;
   int per_xcd;  // logical tiles per XCD
   int rpg;      // rows per weight scale group
+  // split K (large-tile kernel only): workgroup slice p of P covers k-tiles
+  // [p * ktn, min((p + 1) * ktn, K / 128)) and, with P > 1, writes its exact partial
+  // products to part[p][t][n] (int32) instead of the epilogue
+  int P, ktn;
+  int32_t* part;
 };
 
 // Epilogue of one 32 x 32 accumulator block (v_mfma_i32_32x32x32_i8 D layout): the lane
@@ -272,13 +277,16 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 
   const int bid = (int)blockIdx.x;
   const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
-  if (tile >= a.tiles_m * a.tiles_n) return;
-  const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
+  const int mn = a.tiles_m * a.tiles_n;
+  if (tile >= mn * a.P) return;
+  const int sl = tile / mn, tmn = tile - sl * mn;  // K slice; tiles of one slice adjacent
+  const int tm = tmn % a.tiles_m, tn = tmn / a.tiles_m;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int wm = wave / WX, wn = wave % WX;
   const int m0 = tm * BM, n0 = tn * BN;
   const int Kb = a.K >> 2;
-  const int nk = a.K / kPfKT;
+  const int kb = sl * a.ktn;                      // first k-tile of the slice
+  const int nk = min(a.ktn, a.K / kPfKT - kb);    // k-tiles of the slice (>= 1)
   const float beta = a.ws[n0 / a.rpg];
   for (int i = tid; i < BM; i += kPfThreads) {
     const int t = m0 + i;
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 #pragma unroll
   for (int r = 0; r < XQ; ++r) rs[r] = 0;
   auto load_part = [&](Regs& R, int kt, int part) {
-    kt = min(kt, nk - 1);  // past the last k-tile: reload it (in range, never read back)
+    kt = kb + min(kt, nk - 1);  // past the slice's last k-tile: reload it (never read back)
 #pragma unroll
     for (int q = 0; q < NITEM; ++q) {
       if (q * 3 / NITEM != part) continue;
@@ -448,6 +456,24 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
   }
   __syncthreads();
 
+  if (a.P > 1) {
+    // one K slice of several: the exact partial sum_k x q of the slice, rescaled later
+    int32_t* pp = a.part + (int64_t)sl * a.T * a.N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int n = n0 + wn * WN + j * 32 + li;
+        const int tb = wm * WM + i * 32 + 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dt = 8 * (r >> 2) + (r & 3);
+          const int t = m0 + tb + dt;
+          if (t < a.T && n < a.N) pp[(int64_t)t * a.N + n] = acc[i][j][r] - xsum[tb + dt];
+        }
+      }
+    return;
+  }
   const bool full = m0 + BM <= a.T && n0 + BN <= a.N && n0 / a.rpg == (n0 + BN - 1) / a.rpg;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -457,6 +483,26 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
                      fac, xsum, full);
       __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Sum of the P slice partials of a split-K product and the rescale (the same arithmetic
+// as every other epilogue): acc = sum_p part[p][t][n], Y = fp32(acc) * fp32(beta_g / s_t).
+// One thread per four consecutive outputs of a token row; grid.y = token.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(PfArgs a) {
+  const int t = blockIdx.y;
+  const int n_first = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const float xs = a.xs[t];
+  const int64_t plane = (int64_t)a.T * a.N;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int n = n_first + e;
+    if (n >= a.N) break;
+    const int64_t o = (int64_t)t * a.N + n;
+    int v = 0;
+    for (int q = 0; q < a.P; ++q) v += a.part[q * plane + o];
+    a.Y[o] = (float)v * (a.ws[n / a.rpg] / xs);
+    if (a.acc) a.acc[o] = v;
+  }
 }
 
 // Compute units of the current device (queried once).
@@ -474,7 +520,8 @@ inline int pf_cus() {
 }
 
 template <int MI, int NI, int WY, int OCC>
-hipError_t launch_prefill_big(const bl_proj_internal* p, int T, hipStream_t stream) {
+hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* part,
+                              hipStream_t stream) {
   constexpr int BM = 32 * MI * WY, BN = 32 * NI * (4 / WY);
   PfArgs a{};
   a.Xq = p->Xq;
@@ -489,11 +536,33 @@ hipError_t launch_prefill_big(const bl_proj_internal* p, int T, hipStream_t stre
   a.rpg = p->rpg;
   a.tiles_m = (T + BM - 1) / BM;
   a.tiles_n = (p->N + BN - 1) / BN;
-  const int tiles = a.tiles_m * a.tiles_n;
+  const int nkt = p->K / kPfKT;
+  a.ktn = (nkt + P - 1) / P;
+  a.P = (nkt + a.ktn - 1) / a.ktn;  // no empty slice
+  a.part = a.P > 1 ? part : nullptr;
+  const int tiles = a.tiles_m * a.tiles_n * a.P;
   a.per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL((prefill_big_kernel<MI, NI, WY, OCC>), dim3((unsigned)(8 * a.per_xcd)),
                      dim3(kPfThreads), 0, stream, a);
+  if (a.P > 1)
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((a.N + 1023) / 1024), (unsigned)T),
+                       dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+// Split-K plan for a product of T <= 128 tokens on 32*MI x 256 tiles: the number of K
+// slices that gives every CU about one workgroup, keeping at least 8 k-tiles per slice;
+// 1 when the tiles alone fill the device.
+inline int splitk_slices(int T, int N, int K) {
+  if (T > 128 || K % kPfKT) return 1;
+  const int MI = (T + 31) / 32;
+  const int64_t tiles = (int64_t)((T + 32 * MI - 1) / (32 * MI)) * ((N + 255) / 256);
+  const int cus = pf_cus();
+  if (tiles >= cus) return 1;
+  int P = (int)((cus + tiles - 1) / tiles);
+  const int most = (K / kPfKT) / 8;
+  P = P < most ? P : most;
+  return P < 1 ? 1 : P;
 }
 
 template <int BM, int BN>
@@ -524,17 +593,43 @@ using namespace bl;
 
 bool bl_prefill_supports(int T, int K) { return T >= 1 && K % 128 == 0; }
 
-// 128 x 256 tiles (1 x 4 waves of 128 x 64) when they give every CU at least one;
-// two workgroups per CU when there are more tiles than CUs, so that one workgroup's
-// epilogue (the fp32 stores) runs under the other's MFMAs, one otherwise (then the
-// accumulators sit in AGPRs and nothing spills). Smaller problems take the
-// single-stage tiles.
-hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, hipStream_t stream) {
-  const int64_t tiles = (int64_t)((T + 127) / 128) * ((p->N + 255) / 256);
+bool bl_prefill_splits(int T, int N, int K) {
+  const int P = splitk_slices(T, N, K);
+  return P > 1 && (int64_t)((N + 255) / 256) * P * 4 >= (int64_t)pf_cus() * 3;
+}
+
+size_t bl_prefill_scratch_bytes(int T, int N, int K) {
+  const int P = splitk_slices(T, N, K);
+  return P > 1 ? (size_t)P * T * N * sizeof(int32_t) : 0;
+}
+
+// Up to 128 tokens: 32*MI x 256 tiles (1 x 4 waves of 32*MI x 64), with K cut into
+// slices when the tiles alone would leave CUs idle; the slices' exact int32 partials go
+// to the caller's scratch (bl_prefill_scratch_bytes) and a second kernel sums and
+// rescales them. Without that scratch, the single-stage tiles below.
+// Beyond 128 tokens: 128 x 256 tiles when they give every CU at least one; two
+// workgroups per CU when there are more tiles than CUs, so that one workgroup's epilogue
+// (the fp32 stores) runs under the other's MFMAs, one otherwise (then the accumulators
+// sit in AGPRs and nothing spills). Smaller problems take the single-stage tiles.
+hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, int32_t* scratch,
+                             size_t scratch_bytes, hipStream_t stream) {
   const int cus = pf_cus();
+  if (T <= 128) {
+    const int P = splitk_slices(T, p->N, p->K);
+    const bool have = P == 1 || (scratch && scratch_bytes >= bl_prefill_scratch_bytes(T, p->N, p->K));
+    const int MI = (T + 31) / 32;
+    const int64_t tiles = (int64_t)((p->N + 255) / 256) * P;
+    if (have && tiles * 4 >= (int64_t)cus * 3) {
+      if (MI == 1) return launch_prefill_big<1, 2, 1, 2>(p, T, P, scratch, stream);
+      if (MI == 2) return launch_prefill_big<2, 2, 1, 2>(p, T, P, scratch, stream);
+      if (MI == 3) return launch_prefill_big<3, 2, 1, 2>(p, T, P, scratch, stream);
+      return launch_prefill_big<4, 2, 1, 2>(p, T, P, scratch, stream);
+    }
+  }
+  const int64_t tiles = (int64_t)((T + 127) / 128) * ((p->N + 255) / 256);
   if (T >= 128 && tiles >= cus)
-    return tiles > cus ? launch_prefill_big<4, 2, 1, 2>(p, T, stream)
-                       : launch_prefill_big<4, 2, 1, 1>(p, T, stream);
+    return tiles > cus ? launch_prefill_big<4, 2, 1, 2>(p, T, 1, nullptr, stream)
+                       : launch_prefill_big<4, 2, 1, 1>(p, T, 1, nullptr, stream);
   const int64_t big = (int64_t)((T + 255) / 256) * ((p->N + 127) / 128);
   if (T >= 256 && big >= 512) return launch_prefill_t<256, 128>(p, T, stream);
   return launch_prefill_t<128, 128>(p, T, stream);

@@ -59,7 +59,9 @@ def test_header_declares_the_abi():
               "bitlinear_forward_grouped_scale_groups", "bitlinear_warmup_lambda",
               "bitlinear_fake_quant_weights", "bitlinear_fake_quant_acts",
               "bitlinear_rmsnorm_backward", "bitlinear_bitdelta_compress",
-              "bitlinear_bitdelta_forward"]:
+              "bitlinear_bitdelta_forward", "bitlinear_forward_workspace_bytes",
+              "bitlinear_forward_ws", "bitlinear_forward_grouped_ws",
+              "bitlinear_forward_choice_ws"]:
         assert n in names
 
 
@@ -201,14 +203,52 @@ def test_dispatch_choice(lib):
     assert f(1, 4096, 14336) == 1
     assert f(2, 4096, 4096) == 2
     assert f(16, 4096, 4096) == 2
+    # without a workspace the tiled GEMM cannot split K: the streaming kernel up to 95
     assert f(32, 8192, 28672) == 2
-    assert f(33, 8192, 28672) == 2    # passes of 32: the GEMM would have 64 tiles
     assert f(64, 8192, 28672) == 2
-    assert f(128, 28672, 8192) == 2   # 224 GEMM tiles: four passes of 32 tokens
+    assert f(64, 14336, 4096) == 2
+    assert f(96, 4096, 4096) == 3
+    assert f(128, 28672, 8192) == 3
     assert f(129, 28672, 8192) == 3
     assert f(128, 65536, 4096) == 3   # 512 GEMM tiles
     assert f(2048, 14336, 4096) == 3
     assert f(8, 256, 1028) == 4
+
+
+def test_split_k_workspace_query_and_validation(lib):
+    # split-K workspace: one int32 plane [T, N] per K slice, slices chosen so that the
+    # 256-row tiles fill 256 CUs with at least 8 k-tiles of 128 codes each
+    q = lib.bitlinear_forward_workspace_bytes
+    q.argtypes = [I64, I64, I64]
+    q.restype = ctypes.c_size_t
+    assert q(40, 12288, 4096) == 4 * 40 * 12288 * 4     # 48 tiles, 4 slices (32 k-tiles)
+    assert q(64, 8192, 28672) == 8 * 64 * 8192 * 4      # 32 tiles, 8 slices
+    assert q(64, 65536, 4096) == 0                      # 256 tiles: no split
+    assert q(129, 8192, 28672) == 0                     # beyond 128 tokens
+    assert q(0, 8192, 28672) == 0 and q(8, 8192, 4098) == 0
+    c = lib.bitlinear_forward_choice_ws
+    c.argtypes = [I64, I64, I64, ctypes.c_size_t]
+    c.restype = ctypes.c_int
+    for T, N, K, k in [(31, 8192, 28672, 2), (32, 8192, 28672, 3), (64, 8192, 28672, 3),
+                       (32, 28672, 8192, 2), (64, 28672, 8192, 3), (64, 4096, 4096, 2)]:
+        # from 32 tokens at K >= 16384, from 64 when the slices fill the device (112 row
+        # tiles x 3 slices, 32 x 8); 16 row tiles x 4 slices do not
+        assert c(T, N, K, q(T, N, K)) == k, (T, N, K)
+    need = q(64, 14336, 4096)
+    assert c(64, 14336, 4096, need) == 3 and c(64, 14336, 4096, need - 4) == 2
+    plain = lib.bitlinear_forward_choice
+    plain.argtypes = [I64, I64, I64]
+    plain.restype = ctypes.c_int
+    assert c(64, 14336, 4096, 0) == plain(64, 14336, 4096) == 2
+    f = lib.bitlinear_forward_ws
+    f.argtypes = [P, P, I64, I64, P, P, I64, P, P, ctypes.c_int, P, ctypes.c_size_t, P]
+    f.restype = ctypes.c_int
+    A, B, C, D, E = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20   # aligned, never touched
+    assert f(A, B, 40, 4096, C, D, 12288, E, None, 3, (6 << 20) + 8, 1 << 24, None) == BL_ERR_ALIGN
+    g = lib.bitlinear_forward_grouped_ws
+    g.argtypes = [P, ctypes.c_int, I64, P, ctypes.c_size_t, P]
+    g.restype = ctypes.c_int
+    assert g(None, 1, 40, None, 0, None) == BL_ERR_NULL
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

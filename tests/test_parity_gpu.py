@@ -179,6 +179,9 @@ PRODUCT_CASES = [
     # large-tile kernels (chosen by tile count): 128 x 256 tiles, then 256 x 256 tiles,
     # ragged in tokens and rows
     ("prefill", 130, 32845, 256), ("prefill", 300, 49102, 384), ("prefill", 513, 32668, 256),
+    # up to 128 tokens with few row tiles: K cut into slices (int32 partials, then a
+    # summing and rescaling kernel); one token block of 32, 64 (ragged) and 128 rows
+    ("prefill", 17, 6500, 16384), ("prefill", 40, 12288, 4096), ("prefill", 100, 9000, 8192),
     ("generic", 3, 77, 68), ("generic", 5, 300, 4100), ("generic", 1, 16, 4),
 ]
 
@@ -211,6 +214,47 @@ def test_product_extreme_accumulators(bl, kernel, T):
     assert np.array_equal(host(accg), acc_o)
     assert np.abs(acc_o).max() == 127 * K
     assert_y_close(host(Yg), oracle.rescale(acc_o, xs, beta), kernel)
+
+
+def test_splitk_workspace_and_graph_capture(bl):
+    # split K: the slices' int32 partials go to the caller's workspace. With no or too
+    # small a workspace the product runs unsplit; either way it matches the oracle, also
+    # as a captured graph replayed several times with eager work in between.
+    T, N, K = 40, 12288, 4096
+    Xq, P, xs, beta = random_product_inputs(T, N, K, 77)
+    acc_o = oracle.product(Xq, P, K)
+    Y_o = oracle.rescale(acc_o, xs, beta)
+    dXq, dxs, dP = dev(Xq), dev(xs), dev(P)
+    db = dev(np.array([beta], np.float32))
+    nb = bl.bitlinear_forward_workspace_bytes(T, N, K)
+    assert nb > 0
+    Y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    acc = torch.empty((T, N), dtype=torch.int32, device="cuda")
+
+    def check(what):
+        assert np.array_equal(host(acc), acc_o), what
+        assert_y_close(host(Y), Y_o, what)
+
+    for ws in (torch.empty(nb, dtype=torch.uint8, device="cuda"), None,
+               torch.empty(nb - 16, dtype=torch.uint8, device="cuda")):
+        acc.fill_(-1)
+        bl.bitlinear_forward_ws(dXq, dxs, dP, db, Y, acc, "prefill", ws)
+        torch.cuda.synchronize()
+        check("eager, workspace %s" % (None if ws is None else ws.numel()))
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        bl.bitlinear_forward_ws(dXq, dxs, dP, db, Y, acc, "prefill", ws)
+    for rep in range(3):
+        Y.fill_(7.0)
+        acc.fill_(-1)
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check("graph replay %d" % rep)
+    del g
 
 
 def test_kernels_agree_bitwise(bl):

@@ -46,7 +46,8 @@ CASES = [("gemv", 1, 512, 4096, 8), ("gemv", 1, 300, 4096, 3), ("gemv", 1, 96, 1
          ("gemv", 1, 4096, 14336, 8), ("skinny", 5, 512, 4096, 8), ("skinny", 16, 96, 1024, 12),
          ("skinny", 32, 200, 8192, 5), ("prefill", 70, 512, 4096, 8), ("prefill", 300, 300, 1024, 3),
          ("prefill", 130, 96, 1024, 48), ("prefill", 130, 33000, 256, 125),
-         ("prefill", 300, 49140, 256, 195), ("generic", 3, 100, 1028, 4),
+         ("prefill", 300, 49140, 256, 195), ("prefill", 40, 12288, 4096, 96),
+         ("generic", 3, 100, 1028, 4),
          ("auto", 1, 1024, 4096, 1)]
 
 

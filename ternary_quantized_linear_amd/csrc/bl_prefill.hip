@@ -259,6 +259,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
 //     is loaded into one register set while k-tile kt + 1 (loaded during kt - 1) is
 //     staged from the other into the other LDS stage, both spread over the MFMA steps;
 //     one barrier per k-tile.
+//   - Split K (a.P > 1): workgroup tile and slice come from one index (the tiles of a
+//     slice adjacent, so an XCD's workgroups share activation k-tiles); the slice's
+//     exact partial (token sums already subtracted) goes to plane p of a.part, and
+//     splitk_reduce_kernel sums the planes and rescales.
 //
 // Packed LDS row of a k-tile: the eight dwords d0..d7 of the row's 32 bytes (dword d =
 // codes 16d..16d+15) stored as d0 d2 d4 d6 | d1 d3 d5 d7, so that lane half lg reads its

@@ -148,13 +148,13 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   const float4* x4 = reinterpret_cast<const float4*>(e.X + (int64_t)t * e.K);
   const bool has_gain = e.gain != nullptr && !a.no_norm;
   const float4* g4 = reinterpret_cast<const float4*>(e.gain);
-  // the row (and the gain) are loaded once, up front
-  float4 v[VPT], gv[VPT];
+  // the row is loaded once, up front; the gain (shared by every row, so cache-resident)
+  // only where the norm needs it, which keeps it out of the registers that hold the row
+  float4 v[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     int i = threadIdx.x + j * NT;
     v[j] = i < K4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    gv[j] = has_gain && i < K4 ? g4[i] : make_float4(1.f, 1.f, 1.f, 1.f);
   }
   if (!a.no_norm) {
     SumSq4 acc;
@@ -165,8 +165,16 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
     block_dd_sum<NT>(hi, lo, sh_hi, sh_lo);
     const double ss = hi;  // hi + lo is already rounded into hi by dd_add
     const double r = 1.0 / sqrt(ss / (double)e.K + (double)a.eps);
+    if (has_gain) {
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) v[j] = norm4(v[j], r, gv[j], has_gain);
+      for (int j = 0; j < VPT; ++j) {
+        int i = threadIdx.x + j * NT;
+        v[j] = norm4(v[j], r, i < K4 ? g4[i] : make_float4(1.f, 1.f, 1.f, 1.f), true);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) v[j] = norm4(v[j], r, make_float4(1.f, 1.f, 1.f, 1.f), false);
+    }
     if (FQ && e.rinv && threadIdx.x == 0) e.rinv[t] = r;
   } else if (FQ && e.rinv && threadIdx.x == 0) {
     e.rinv[t] = 1.0;
@@ -264,7 +272,7 @@ hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStre
   else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ>), grid, dim3(256), 0, stream, a);
   else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ>), grid, dim3(256), 0, stream, a);
   else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<256, 8, FQ>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<256, 16, FQ>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ>), grid, dim3(512), 0, stream, a);
   else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ>), grid, dim3(512), 0, stream, a);
   else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);
   return hipGetLastError();

@@ -491,21 +491,37 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 
 // Sum of the P slice partials of a split-K product and the rescale (the same arithmetic
 // as every other epilogue): acc = sum_p part[p][t][n], Y = fp32(acc) * fp32(beta_g / s_t).
-// One thread per four consecutive outputs of a token row; grid.y = token.
+// One thread per four consecutive outputs of a token row (grid.y = token), read and
+// written as 16-byte vectors when N % 4 == 0 (every base pointer is 16-byte aligned).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(PfArgs a) {
   const int t = blockIdx.y;
-  const int n_first = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= a.N) return;
   const float xs = a.xs[t];
   const int64_t plane = (int64_t)a.T * a.N;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int n = n_first + e;
-    if (n >= a.N) break;
-    const int64_t o = (int64_t)t * a.N + n;
+  const int64_t o = (int64_t)t * a.N + n;
+  if ((a.N & 3) == 0) {
+    int4 v = make_int4(0, 0, 0, 0);
+    for (int q = 0; q < a.P; ++q) {
+      const int4 w = *reinterpret_cast<const int4*>(a.part + q * plane + o);
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    const float4 y = make_float4((float)v.x * (a.ws[n / a.rpg] / xs),
+                                 (float)v.y * (a.ws[(n + 1) / a.rpg] / xs),
+                                 (float)v.z * (a.ws[(n + 2) / a.rpg] / xs),
+                                 (float)v.w * (a.ws[(n + 3) / a.rpg] / xs));
+    *reinterpret_cast<float4*>(a.Y + o) = y;
+    if (a.acc) *reinterpret_cast<int4*>(a.acc + o) = v;
+    return;
+  }
+  for (int e = 0; e < 4 && n + e < a.N; ++e) {
     int v = 0;
-    for (int q = 0; q < a.P; ++q) v += a.part[q * plane + o];
-    a.Y[o] = (float)v * (a.ws[n / a.rpg] / xs);
-    if (a.acc) a.acc[o] = v;
+    for (int q = 0; q < a.P; ++q) v += a.part[q * plane + o + e];
+    a.Y[o + e] = (float)v * (a.ws[(n + e) / a.rpg] / xs);
+    if (a.acc) a.acc[o + e] = v;
   }
 }
 

@@ -184,6 +184,7 @@ PRODUCT_CASES = [
     # up to 128 tokens with few row tiles: K cut into slices (int32 partials, then a
     # summing and rescaling kernel); one token block of 32, 64 (ragged) and 128 rows
     ("prefill", 17, 6500, 16384), ("prefill", 40, 12288, 4096), ("prefill", 100, 9000, 8192),
+    ("prefill", 33, 6501, 16384),  # N % 4 != 0: the summing kernel's scalar path
     ("generic", 3, 77, 68), ("generic", 5, 300, 4100), ("generic", 1, 16, 4),
 ]
 

@@ -259,11 +259,16 @@ hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStre
   dim3 grid((unsigned)T, (unsigned)count);
   const int f4 = (maxK + 3) / 4;  // float4 per row
   if (T <= 64) {
-    // few rows: latency-bound, so spread each row over 1024 lanes
-    if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<1024, 1, FQ>), grid, dim3(1024), 0, stream, a);
-    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<1024, 2, FQ>), grid, dim3(1024), 0, stream, a);
-    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<1024, 4, FQ>), grid, dim3(1024), 0, stream, a);
-    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<1024, 8, FQ>), grid, dim3(1024), 0, stream, a);
+    // Few rows: latency-bound, each row on one CU, whose four SIMDs do all of its fp64
+    // arithmetic. The fewest waves that hold the row: every wave repeats the block
+    // reductions, so 512 lanes beat 1024 (4-input decode call 4.6 us against 5.3 us,
+    // same bits), and 256 lanes suit rows of up to 4096 (2.8 us against 3.1).
+    if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ>), grid, dim3(256), 0, stream, a);
+    else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ>), grid, dim3(256), 0, stream, a);
+    else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ>), grid, dim3(256), 0, stream, a);
+    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<512, 4, FQ>), grid, dim3(512), 0, stream, a);
+    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ>), grid, dim3(512), 0, stream, a);
+    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ>), grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
   }

@@ -109,7 +109,8 @@ def test_quantize_weights_special_cases(bl):
 @pytest.mark.parametrize("T,K,dist", [(8, 1024, "n"), (3, 4100, "n"), (1, 4096, "n"),
                                       (1, 14336, "n"), (16, 4096, "t"), (5, 28672, "n"),
                                       (2, 40000, "n"), (64, 8192, "t"), (7, 132104, "t"),
-                                      (66, 14336, "t"), (130, 2052, "n"), (200, 28672, "n")])
+                                      (66, 14336, "t"), (130, 2052, "n"), (200, 28672, "n"),
+                                      (4, 2000, "n"), (1, 28000, "t"), (2, 6000, "t")])
 def test_quantize_acts_parity(bl, T, K, dist):
     X = (workloads.acts_normal if dist == "n" else workloads.acts_student_t)(T, K, T + K)
     q, s = oracle.quantize_acts(X)

@@ -129,12 +129,17 @@ __device__ __forceinline__ float4 norm4(float4 x, double r, float4 g, bool has_g
                      norm_one(x.z, r, g.z, has_gain), norm_one(x.w, r, g.w, has_gain));
 }
 
+// Four codes clamp(round(y * s), -128, 127) as bytes. The clamp comes first (its bounds
+// are integers, so the order does not change the result); adding 1.5 * 2^23 then rounds
+// to the nearest integer, ties to even, and leaves its two's-complement byte in the low
+// byte of the sum's bits (the spacing of floats in [2^23, 2^24) is 1).
 __device__ __forceinline__ uint32_t quant4(float4 y, float s) {
   auto q = [&](float v) -> uint32_t {
-    float t = fminf(fmaxf(rintf(v * s), -128.0f), 127.0f);
-    return (uint32_t)((int)t & 0xFF);
+    return __float_as_uint(__builtin_amdgcn_fmed3f(v * s, -128.0f, 127.0f) + 12582912.0f);
   };
-  return q(y.x) | (q(y.y) << 8) | (q(y.z) << 16) | (q(y.w) << 24);
+  const uint32_t lo = __builtin_amdgcn_perm(q(y.y), q(y.x), 0x0C0C0400u);  // x, y, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(q(y.w), q(y.z), 0x04000C0Cu);  // 0, 0, z, w
+  return lo | hi;
 }
 
 // Row held in registers: lane i owns float4 i, i+NT, ..., i+(VPT-1)NT of the row.

@@ -191,18 +191,8 @@ bool bl_bitdelta_supports(int64_t N, int64_t M, int B) {
 hipError_t bl_launch_bitdelta(const uint16_t* base, const uint8_t* D, const float* alpha,
                               const float* X, float* Y, int64_t N, int64_t M, int B,
                               hipStream_t stream) {
-  static int cap = 0;
-  if (cap == 0) {
-    int dev = 0, cus = 256, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bitdelta_kernel, kBdThreads, 4096) !=
-            hipSuccess ||
-        per < 1)
-      per = 1;
-    cap = cus * per;
-  }
+  static int cap_slot = 0;
+  const int cap = bl_resident_wgs((const void*)bitdelta_kernel, kBdThreads, 4096, 1, &cap_slot);
   BdArgs a{};
   a.base = base;
   a.D = D;

@@ -7,6 +7,32 @@
 
 #include "bl_internal.h"
 
+int bl_device_cus() {
+  static int cached = 0;
+  int v = __atomic_load_n(&cached, __ATOMIC_RELAXED);
+  if (v > 0) return v;
+  int dev = 0, n = 0;
+  v = hipGetDevice(&dev) == hipSuccess &&
+              hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+              n > 0
+          ? n
+          : 256;
+  __atomic_store_n(&cached, v, __ATOMIC_RELAXED);
+  return v;
+}
+
+int bl_resident_wgs(const void* kernel, int threads, size_t lds, int fallback, int* slot) {
+  int v = __atomic_load_n(slot, __ATOMIC_RELAXED);
+  if (v > 0) return v;
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, lds) != hipSuccess ||
+      per < 1)
+    per = fallback;
+  v = bl_device_cus() * per;
+  __atomic_store_n(slot, v, __ATOMIC_RELAXED);
+  return v;
+}
+
 namespace {
 
 thread_local char g_last_error[256] = "";

@@ -406,21 +406,8 @@ GemvCfg gemv_cfg(int C) {
 template <int FMT>
 int gemv_resident(bool big, size_t lds) {
   static int cached[2] = {0, 0};
-  if (cached[big]) return cached[big];
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-  }
-  int per = 0;
   const void* f = big ? (const void*)gemv_kernel<2, FMT> : (const void*)gemv_kernel<1, FMT>;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, kGemvThreads, lds) != hipSuccess ||
-      per < 1)
-    per = 2;
-  cached[big] = cus * per;
-  return cached[big];
+  return bl_resident_wgs(f, kGemvThreads, lds, 2, &cached[big ? 1 : 0]);
 }
 
 }  // namespace bl

@@ -21,6 +21,15 @@ struct bl_proj_internal {
   int rpg;  // rows per weight scale group: row o uses w_scale[o / rpg] (rpg = N: one scale)
 };
 
+// Compute units of the current device, queried once per process and cached (the
+// library targets one part, so every device it runs on has the same count). Safe to
+// call from several threads: a race only repeats the query and stores the same value.
+int bl_device_cus();
+// Resident workgroups of `kernel` with `threads` threads and `lds` dynamic LDS bytes
+// (the occupancy query times bl_device_cus(); `fallback` per CU if the query fails),
+// cached in `slot`; the same thread-safety as bl_device_cus.
+int bl_resident_wgs(const void* kernel, int threads, size_t lds, int fallback, int* slot);
+
 size_t bl_weight_workspace_bytes_impl(int64_t N, int64_t K);
 hipError_t bl_launch_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* P,
                                       float* w_scale, double* w_gamma, void* ws,

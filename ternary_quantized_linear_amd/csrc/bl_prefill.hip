@@ -525,19 +525,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(PfArgs a) {
   }
 }
 
-// Compute units of the current device (queried once).
-inline int pf_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
+inline int pf_cus() { return bl_device_cus(); }
 
 template <int MI, int NI, int WY, int OCC>
 hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* part,

@@ -333,21 +333,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   }
 }
 
+// (always asked with the same LDS size, so one cached value per instance)
 template <int TB>
 int sk_resident(size_t lds) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-  }
-  int per = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, skinny_kernel<TB>, kSkThreads, lds) !=
-          hipSuccess ||
-      per < 1)
-    per = 1;
-  return cus * per;
+  static int cached = 0;
+  return bl_resident_wgs((const void*)skinny_kernel<TB>, kSkThreads, lds, 1, &cached);
 }
 
 // Segment length and team shape for K: the largest fraction of wave-steps spent on real

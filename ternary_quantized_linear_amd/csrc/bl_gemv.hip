@@ -457,6 +457,18 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
   // three (2-bit) or four (1-bit) row groups in flight, keeps HBM as busy as a full
   // round with fewer waves to start and to drain (measured: 3% faster than a full round
   // on the 8B decode layer, 5% on its 1-bit form, 4-15% on the 70B projections).
+  // A partition dispatched later gets its first rows later (its ring loads queue
+  // behind those of the partitions before it), so in the 2-bit form each partition's
+  // cost is raised by the fraction of the total dispatched before it: later partitions
+  // get more workgroups and fewer rows per wave (measured 1.5-3% on the 8B layer; the
+  // 1-bit form, whose waves spend longer on their activations, measured 5% slower).
+  int64_t wcost[BL_GROUP_CAP], wtotal = 0, before = 0;
+  for (int o = 0; o < count; ++o) {
+    const int64_t c = cost[order[o]];
+    wcost[o] = FMT == 0 ? c + (int64_t)((double)c * (double)before / (double)total) : c;
+    before += c;
+    wtotal += wcost[o];
+  }
   const int resident = gemv_resident<FMT>(big, 4096);
   const int cap = resident / 2;
   int wgs = 0, slots = 0;
@@ -477,7 +489,7 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     g.rpg = p[i].rpg;
     const int groups = (g.N + c.RW - 1) / c.RW;
     const int gpw = kGemvWaves / c.S;
-    int64_t n = (cost[i] * (int64_t)(cap - count) + total - 1) / total;
+    int64_t n = (wcost[o] * (int64_t)(cap - count) + wtotal - 1) / wtotal;
     n = n < 1 ? 1 : n;
     const int64_t most = (groups + gpw - 1) / gpw;
     n = n > most ? most : n;

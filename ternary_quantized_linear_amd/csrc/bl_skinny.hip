@@ -16,9 +16,14 @@
 //   - Per wave and segment, the MFMA B operands (16 tokens x 64 codes each: lane (token
 //     t, k-slot g) holds 16 activation bytes) live in registers for the whole sweep.
 //     They are 4x4 byte-transposed to the order in which a packed dword unpacks, and
-//     the code -> k-slot assignment is chosen so that a lane's own 128-bit weight load
-//     (row lane % 16, bytes 64m + 16g of the segment) is directly the A operand of four
-//     MFMAs: no cross-lane exchange of weights.
+//     the code -> k-slot assignment is chosen so that the 16 packed bytes of row
+//     lane % 16 at bytes 64m + 16g of the segment are directly the A operand of four
+//     MFMAs.
+//   - Those 16 rows x 64 bytes are not what a wave loads: every load instruction reads
+//     contiguous 16-byte pieces (the wave's segment of row 0, then of row 1, ...), and
+//     the wave moves them through its own LDS area (rows padded by 16 bytes) into the
+//     MFMA layout. Loading the 16-row layout directly (16 pieces of 64 bytes, one per
+//     row, per instruction) measured 8-9% slower at 8-32 tokens.
 //   - A team sweeps its row blocks (16 rows each); per row block every wave loads 16
 //     rows x 64*MPW bytes with MPW 128-bit buffer loads per lane, kept in a ring D row
 //     blocks deep (non-temporal; rows past N and codes past K fall outside the buffer
@@ -47,6 +52,10 @@ constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;  // 512
 constexpr int kSkTileKB = 96;  // LDS for the partial tiles of a workgroup's row blocks, KiB
 constexpr size_t kSkLdsMax = kSkTileKB * 1024 + 96 * 4 + 32 * 4;
+constexpr int kSkLdsCU = 160 * 1024;  // LDS of one CU, all of it one workgroup's
+// per-wave weight regroup areas: 16 rows of 64 * MPW + 16 bytes, sized for MPW = 7
+constexpr size_t kSkRegroup = (size_t)kSkWaves * 16 * (64 * 7 + 16);
+static_assert(kSkLdsMax + 16 + kSkRegroup <= (size_t)kSkLdsCU, "LDS plan exceeds a CU");
 
 struct SkProj {
   const int8_t* Xq;
@@ -71,6 +80,7 @@ struct SkArgs {
   SkProj p[BL_GROUP_CAP];
   int count;
   int T;
+  int wbase;  // byte offset of the per-wave weight regroup areas in dynamic LDS
 };
 
 typedef const SkArgs __attribute__((address_space(4)))* SkArgsPtr;
@@ -116,7 +126,9 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 
 template <int TB, int MPW, int D>
 __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wave, int* tiles,
-                                         int* counts, const float* facs) {
+                                         int* counts, const float* facs, uint8_t* wlds) {
+  constexpr int RS = 64 * MPW + 16;  // LDS bytes per row of the wave's regroup area
+  constexpr int PPR = 4 * MPW;       // 16-byte pieces per row segment
   const int lane = threadIdx.x & (kWave - 1), li = lane & 15, lg = lane >> 4;
   const int S = P.S, teams = P.teams;
   const int team = wave / S;
@@ -180,7 +192,10 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
 
   // weight ring: row block rb as a buffer of its (up to) 16 rows, empty past the matrix;
   // the prefetch position (pass, row-block ordinal) advances per load
+  // Load m of a row block: piece f = 64m + lane of the wave's 16 x PPR pieces (row f / PPR,
+  // piece f % PPR of the row's segment), so each instruction reads contiguous bytes.
   uint4 w[D][MPW];
+  uint8_t* const wl = wlds + wave * 16 * RS;
   int fn = 0, fr = 0, fp = 0;
   auto load_w = [&](int d) {
     const int rb = tg + fr * TT;
@@ -190,8 +205,10 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
     const Rsrc wr = make_rsrc(P.W + (valid ? (int64_t)rb * 16 * Kb : 0), (uint32_t)(rows * Kb));
 #pragma unroll
     for (int m = 0; m < MPW; ++m) {
-      const int byte = (sg * MPW + m) * 64 + 16 * lg;
-      const uint32_t off = byte < Kb ? (uint32_t)(li * Kb + byte) : kOob;
+      const int f = m * kWave + lane;
+      const int r = f / PPR, c = f - (f / PPR) * PPR;
+      const int byte = sg * MPW * 64 + 16 * c;
+      const uint32_t off = byte < Kb ? (uint32_t)(r * Kb + byte) : kOob;
       const v4i v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // non-temporal
       w[d][m] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
     }
@@ -215,9 +232,23 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
     v4i acc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[tb] = ncs[tb];
+    // the loaded pieces into the wave's LDS rows, then back in the MFMA layout (row li,
+    // bytes 64m + 16lg); the wavefront fences keep the reads after every lane's writes
 #pragma unroll
     for (int m = 0; m < MPW; ++m) {
-      const uint32_t wd[4] = {w[d][m].x, w[d][m].y, w[d][m].z, w[d][m].w};
+      const int f = m * kWave + lane;
+      const int r = f / PPR, c = f - (f / PPR) * PPR;
+      *reinterpret_cast<uint4*>(wl + r * RS + 16 * c) = w[d][m];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint4 wa[MPW];
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) wa[m] = *reinterpret_cast<const uint4*>(wl + li * RS + 64 * m + 16 * lg);
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const uint32_t wd[4] = {wa[m].x, wa[m].y, wa[m].z, wa[m].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t u[4];
@@ -323,12 +354,13 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   }
   __syncthreads();
   if (wave >= P.S * P.teams) return;  // leftover waves: no segment (no barrier follows)
+  uint8_t* const wlds = reinterpret_cast<uint8_t*>(sk_lds) + a->wbase;
   switch (P.mpw) {
-    case 1: sk_sweep<TB, 1, 4>(P, T, wgl, wave, tiles, counts, facs); break;
-    case 2: sk_sweep<TB, 2, 4>(P, T, wgl, wave, tiles, counts, facs); break;
-    case 4: sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs); break;
+    case 1: sk_sweep<TB, 1, 4>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
+    case 2: sk_sweep<TB, 2, 4>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
+    case 4: sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
     default:
-      if constexpr (TB == 1) sk_sweep<TB, 7, 2>(P, T, wgl, wave, tiles, counts, facs);
+      if constexpr (TB == 1) sk_sweep<TB, 7, 2>(P, T, wgl, wave, tiles, counts, facs, wlds);
       break;
   }
 }
@@ -370,7 +402,7 @@ void sk_plan(int K, int TB, SkProj& s) {
 template <int TB>
 hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)skinny_kernel<TB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSkLdsMax);
+      (const void*)skinny_kernel<TB>, hipFuncAttributeMaxDynamicSharedMemorySize, kSkLdsCU);
   if (attr != hipSuccess) return attr;
   SkArgs a{};
   int64_t total = 0;
@@ -389,8 +421,8 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
     sk_plan(p[i].K, TB, s);
     total += (int64_t)p[i].N * (p[i].K / 4);
   }
-  // the occupancy does not depend on the LDS size up to the cap (registers bound it)
-  const int cap = sk_resident<TB>(kSkLdsMax);
+  // one workgroup per CU: its registers and, with the regroup areas, its LDS bound it
+  const int cap = sk_resident<TB>(kSkLdsMax + 16 + kSkRegroup);
   int wgs = 0;
   size_t lds = 0;
   for (int i = 0; i < count; ++i) {
@@ -420,6 +452,8 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.T = T;
+  a.wbase = (int)((lds + 15) / 16 * 16);
+  lds = (size_t)a.wbase + kSkRegroup;
   hipLaunchKernelGGL(skinny_kernel<TB>, dim3((unsigned)wgs), dim3(kSkThreads), lds, stream, a);
   return hipGetLastError();
 }

@@ -35,7 +35,7 @@ MIS = P(0x100004)    # misaligned
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        import __graft_entry__  # noqa: F401  (build it the way the driver does)
+        import __graft_entry__  # noqa: F401  (the library is not built yet: build it)
         __graft_entry__.build()
     return ctypes.CDLL(LIB)
 

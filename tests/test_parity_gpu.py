@@ -177,6 +177,10 @@ PRODUCT_CASES = [
     ("skinny", 9, 77, 4352), ("prefill", 33, 130, 1024), ("prefill", 64, 200, 28672),
     ("skinny", 33, 130, 1024), ("skinny", 100, 200, 4096), ("skinny", 128, 64, 8192),
     ("skinny", 8, 64, 256),
+    # every segment length of the LDS regroup (64*MPW bytes per row, MPW = 1, 2, 4, 7),
+    # one and two token blocks, several passes over K, ragged rows
+    ("skinny", 12, 45, 512), ("skinny", 20, 45, 512), ("skinny", 16, 77, 28672),
+    ("skinny", 7, 19, 4096), ("skinny", 2, 1001, 14336),
     ("prefill", 1, 130, 1024), ("prefill", 100, 300, 4096), ("prefill", 129, 129, 1280),
     ("prefill", 263, 520, 14336), ("prefill", 256, 256, 128),
     # large-tile kernels (chosen by tile count): 128 x 256 tiles, then 256 x 256 tiles,

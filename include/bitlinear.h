@@ -107,8 +107,10 @@ bl_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
  * RMSNorm; [HF-1.58] "How quantization works", activations: a norm before the
  * quantizer, absmax per token into [-128, 127]; [bitnet.cpp] "2. Activation
  * quantization", gamma = ||x||_inf and an epsilon). Per token t:
- *   ss  = sum_k x_k^2 in fp64 (each square exact; double-double accumulation,
- *         rounded once)
+ *   ss  = sum_k x_k^2 in fp64 (each square exact; accumulated in double-double
+ *         and returned as the rounded sum of its two parts: the correctly rounded
+ *         sum except when the exact sum lies within about 2^-100 (relative) of a
+ *         rounding midpoint)
  *   r   = 1 / sqrt(ss / K + eps) in fp64 (IEEE division and square root)
  *   y_k = fp32((x_k * r) * g_k), both products in fp64 (no g product when gain is NULL)
  *   s_t = 127 / max(max_k |y_k|, 1e-5) in fp32

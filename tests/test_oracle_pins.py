@@ -290,6 +290,49 @@ def test_act_special_rows():
     assert np.all(q[2] == 0) and s[2] == F32(127.0) / F32(1e-5)   # zero row: floor 1e-5
 
 
+def _decimal_rms_inv(x, eps):
+    # r = 1 / sqrt(mean(x^2) + eps), every step in 60 digits from the exact fp32 inputs
+    getcontext().prec = 60
+    d = [Decimal(float(v)) for v in x]
+    return 1 / (sum(v * v for v in d) / len(d) + Decimal(float(F32(eps)))).sqrt()
+
+
+def test_rms_inv_exact_cases():
+    # x = [3, 4], eps = 0: mean square 25/2, so r = 1/sqrt(12.5) = sqrt(2)/5
+    getcontext().prec = 60
+    r = oracle.rms_inv(np.array([[3.0, 4.0], [2.0, -2.0]], np.float32), eps=0.0)
+    assert r.dtype == np.float64 and r.shape == (2,)
+    exact = Decimal(2).sqrt() / 5
+    assert abs(Decimal(float(r[0])) - exact) <= Decimal(2.0 ** -53) * exact
+    assert r[1] == 0.5                                  # mean square 4: r = 1/2 exactly
+    # the norm switched off: r = 1 for every token, whatever the values
+    X = workloads.acts_normal(3, 64, 5)
+    assert np.array_equal(oracle.rms_inv(X, flags=oracle.NO_NORM), np.ones(3))
+
+
+@pytest.mark.parametrize("K", [4, 96, 4096])
+def test_rms_inv_against_decimal(K):
+    # the fp64 factor is within a few roundings (sum once, /K, +eps, sqrt, 1/) of the
+    # 60-digit value: a K-1 for K, eps outside the square root, eps dropped or taken as
+    # the double 1e-6 instead of fp32(1e-6), or an fp32 square root each miss by far more
+    X = workloads.acts_normal(4, K, 40 + K)
+    X[1] *= F32(1e-3)          # mean square near eps: eps is half of the radicand
+    X[2] *= F32(3e-5)          # mean square far below eps: eps dominates
+    X[3] *= F32(1e4)           # large values
+    r = oracle.rms_inv(X, eps=1e-6)
+    for t in range(X.shape[0]):
+        re = _decimal_rms_inv(X[t], 1e-6)
+        assert abs(Decimal(float(r[t])) - re) <= Decimal(4 * 2.0 ** -53) * re
+
+
+def test_rms_inv_matches_the_rmsnorm_output():
+    # the C RMSNorm forms y = fp32(fp64(x * r)) (unit gain): the same r, bit for bit
+    X = np.concatenate([workloads.acts_normal(4, 1024, 6), workloads.acts_student_t(4, 1024, 7)])
+    r = oracle.rms_inv(X, eps=1e-6)
+    y = (X.astype(np.float64) * r[:, None]).astype(np.float32)
+    assert np.array_equal(y, oracle.rmsnorm(X, None, 1e-6))
+
+
 def test_act_quant_scale_invariance_without_eps():
     # with eps = 0, RMSNorm is invariant under x -> 2^k x, bit for bit
     X = workloads.acts_normal(4, 512, 3)

@@ -131,6 +131,124 @@ def _stream(t, stream=None):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+# ---------------------------------------------------------------- argument checks
+# The C ABI sees raw pointers and sizes; the sizes it gets are taken from these tensors.
+# So before any call, every tensor must have the dtype the ABI reads through its pointer,
+# be contiguous (the ABI assumes dense row-major arrays), sit on the same GPU, and agree
+# with the sizes passed: a short or strided buffer would otherwise be read or written
+# past its end on the device.
+
+_U8, _I8, _I16, _I32 = torch.uint8, torch.int8, torch.int16, torch.int32
+_F32, _F64, _BF16 = torch.float32, torch.float64, torch.bfloat16
+
+
+def _arg(t, name, dtypes, shape=None, numel=None, optional=False):
+    """Checks one tensor argument (None is allowed only when optional)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected %s"
+                         % (name, t.dtype, " or ".join(str(d) for d in dtypes)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (got strides %s for shape %s)"
+                         % (name, tuple(t.stride()), tuple(t.shape)))
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if numel is not None and t.numel() != int(numel):
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), int(numel)))
+
+
+def _dims(t, name, nd):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if t.dim() != nd:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, nd, tuple(t.shape)))
+    return tuple(int(v) for v in t.shape)
+
+
+def _same_gpu(*tensors):
+    """Every given tensor on one GPU (checked after dtypes and shapes)."""
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU, got device %s" % dev)
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check_proj(Xq, x_scale, W, w_scale, Y, acc, codes_per_byte=4, n_scales=1, T=None):
+    """A product's arguments: Xq int8 [T, K], x_scale fp32 [T], W uint8 [N, K/cpb],
+    w_scale fp32 [n_scales], Y fp32 [T, N], acc int32 [T, N] or None -> (T, N, K)."""
+    T0, K = _dims(Xq, "Xq", 2)
+    if T is not None and T0 != T:
+        raise ValueError("Xq has %d tokens, the call is for %d" % (T0, T))
+    N, kb = _dims(W, "W_packed", 2)
+    _arg(Xq, "Xq", _I8)
+    if K % codes_per_byte or kb != K // codes_per_byte:
+        raise ValueError("W_packed has %d bytes per row; K = %d needs %s"
+                         % (kb, K, "K / %d" % codes_per_byte))
+    _arg(W, "W_packed", _U8)
+    _arg(x_scale, "x_scale", _F32, numel=T0)
+    _arg(w_scale, "w_scale", _F32, numel=n_scales)
+    _arg(Y, "Y", _F32, numel=T0 * N)
+    _arg(acc, "acc", _I32, numel=T0 * N, optional=True)
+    _same_gpu(Xq, x_scale, W, w_scale, Y, acc)
+    return T0, N, K
+
+
+def _check_entries(entries, T, codes_per_byte=4, groups=None):
+    if len(entries) < 1 or len(entries) > MAX_GROUP:
+        raise ValueError("a grouped call takes 1..%d entries, got %d" % (MAX_GROUP, len(entries)))
+    dev = None
+    for i, (Xq, xs, Wp, ws, Y, acc) in enumerate(entries):
+        n_scales = 1 if groups is None else int(groups[i])
+        _check_proj(Xq, xs, Wp, ws, Y, acc, codes_per_byte, n_scales, T)
+        dev = Xq.device if dev is None else dev
+        if Xq.device != dev:
+            raise ValueError("grouped entries on different devices: %s and %s" % (dev, Xq.device))
+
+
+def _check_act_entries(entries, T):
+    if len(entries) < 1 or len(entries) > MAX_GROUP:
+        raise ValueError("a grouped call takes 1..%d entries, got %d" % (MAX_GROUP, len(entries)))
+    dev = None
+    for X, gain, Xq, xs in entries:
+        T0, K = _dims(X, "X", 2)
+        if T0 != T:
+            raise ValueError("X has %d tokens, the call is for %d" % (T0, T))
+        _arg(X, "X", _F32)
+        _arg(gain, "gain", _F32, numel=K, optional=True)
+        _arg(Xq, "Xq", _I8, shape=(T, K))
+        _arg(xs, "x_scale", _F32, numel=T)
+        _same_gpu(X, gain, Xq, xs)
+        dev = X.device if dev is None else dev
+        if X.device != dev:
+            raise ValueError("grouped entries on different devices: %s and %s" % (dev, X.device))
+
+
+def _check_weights(W, out, codes_per_byte, scales, scale_name, gamma, workspace):
+    N, K = _dims(W, "W", 2)
+    _arg(W, "W", _F32)
+    if K % codes_per_byte:
+        raise ValueError("K = %d is not a multiple of %d" % (K, codes_per_byte))
+    _arg(out, "W_packed", _U8, shape=(N, K // codes_per_byte))
+    _arg(scales[0], scale_name, _F32, numel=scales[1])
+    _arg(gamma, "w_gamma", _F64, numel=scales[1], optional=True)
+    _arg(workspace, "workspace", _U8)
+    _same_gpu(W, out, scales[0], gamma, workspace)
+    return N, K
+
+
 # ---------------------------------------------------------------- C ABI mirror
 
 def bitlinear_status_str(status: int) -> str:
@@ -150,20 +268,21 @@ def bitlinear_weight_workspace_bytes(N: int, K: int) -> int:
 
 
 def bitlinear_quantize_weights(W, W_packed, w_scale, w_gamma, workspace, stream=None):
-    N, K = W.shape
+    N, K = _check_weights(W, W_packed, 4, (w_scale, 1), "w_scale", w_gamma, workspace)
     _check(_c_qw(_ptr(W), N, K, _ptr(W_packed), _ptr(w_scale), _ptr(w_gamma), _ptr(workspace),
-                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                 _stream(W, stream)), "bitlinear_quantize_weights")
+                 _nbytes(workspace), _stream(W, stream)), "bitlinear_quantize_weights")
 
 
 def bitlinear_quantize_acts(X, gain, eps, flags, Xq, x_scale, stream=None):
-    T, K = X.shape
+    T, K = _dims(X, "X", 2)
+    _check_act_entries([(X, gain, Xq, x_scale)], T)
     _check(_c_qa(_ptr(X), _ptr(gain), T, K, float(eps), int(flags), _ptr(Xq), _ptr(x_scale),
                  _stream(X, stream)), "bitlinear_quantize_acts")
 
 
 def bitlinear_quantize_acts_grouped(entries, T, eps, flags, stream=None):
     """entries: list of (X, gain, Xq, x_scale)."""
+    _check_act_entries(entries, T)
     arr = (_ActDesc * len(entries))()
     for i, (X, gain, Xq, xs) in enumerate(entries):
         arr[i] = _ActDesc(X.data_ptr(), None if gain is None else gain.data_ptr(), Xq.data_ptr(),
@@ -173,16 +292,14 @@ def bitlinear_quantize_acts_grouped(entries, T, eps, flags, stream=None):
 
 
 def bitlinear_forward(Xq, x_scale, W_packed, w_scale, Y, acc=None, stream=None):
-    T, K = Xq.shape
-    N = W_packed.shape[0]
+    T, N, K = _check_proj(Xq, x_scale, W_packed, w_scale, Y, acc)
     _check(_c_fw(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, _ptr(Y),
                  _ptr(acc), _stream(Xq, stream)), "bitlinear_forward")
 
 
 def bitlinear_forward_ex(Xq, x_scale, W_packed, w_scale, Y, acc=None, kernel="auto",
                          stream=None):
-    T, K = Xq.shape
-    N = W_packed.shape[0]
+    T, N, K = _check_proj(Xq, x_scale, W_packed, w_scale, Y, acc)
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     _check(_c_fwx(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, _ptr(Y),
                   _ptr(acc), k, _stream(Xq, stream)), "bitlinear_forward_ex")
@@ -199,10 +316,11 @@ def _workspace(nbytes, like):
 
 def bitlinear_forward_ws(Xq, x_scale, W_packed, w_scale, Y, acc=None, kernel="auto",
                          workspace=None, stream=None):
-    T, K = Xq.shape
-    N = W_packed.shape[0]
+    T, N, K = _check_proj(Xq, x_scale, W_packed, w_scale, Y, acc)
+    _arg(workspace, "workspace", _U8, optional=True)
+    _same_gpu(Xq, workspace)
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    nb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    nb = _nbytes(workspace)
     _check(_c_fw_ws(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, _ptr(Y),
                     _ptr(acc), k, _ptr(workspace), nb, _stream(Xq, stream)),
            "bitlinear_forward_ws")
@@ -219,32 +337,29 @@ def bitlinear_forward_choice(T: int, N: int, K: int, workspace: bool = True) -> 
 
 def bitlinear_forward_grouped(entries, T, stream=None):
     """entries: list of (Xq, x_scale, W_packed, w_scale, Y, acc_or_None)."""
-    arr = (_ProjDesc * len(entries))()
-    for i, (Xq, xs, Wp, ws, Y, acc) in enumerate(entries):
-        arr[i] = _ProjDesc(Xq.data_ptr(), xs.data_ptr(), Wp.data_ptr(), ws.data_ptr(),
-                           Y.data_ptr(), None if acc is None else acc.data_ptr(),
-                           Wp.shape[0], Xq.shape[-1])
-    _check(_c_fwg(arr, len(entries), T, _stream(entries[0][0], stream)),
+    _check_entries(entries, T)
+    _check(_c_fwg(_proj_array(entries), len(entries), T, _stream(entries[0][0], stream)),
            "bitlinear_forward_grouped")
 
 
 def bitlinear_forward_grouped_ws(entries, T, workspace, stream=None):
     """bitlinear_forward_grouped with a split-K workspace (a uint8 tensor or None)."""
-    nb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check_entries(entries, T)
+    _arg(workspace, "workspace", _U8, optional=True)
+    _same_gpu(entries[0][0], workspace)
+    nb = _nbytes(workspace)
     _check(_c_fwg_ws(_proj_array(entries), len(entries), T, _ptr(workspace), nb,
                      _stream(entries[0][0], stream)), "bitlinear_forward_grouped_ws")
 
 
 def bitlinear_quantize_weights_sign(W, W_bits, w_scale, w_alpha, workspace, stream=None):
-    N, K = W.shape
+    N, K = _check_weights(W, W_bits, 8, (w_scale, 1), "w_scale", w_alpha, workspace)
     _check(_c_qws(_ptr(W), N, K, _ptr(W_bits), _ptr(w_scale), _ptr(w_alpha), _ptr(workspace),
-                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                  _stream(W, stream)), "bitlinear_quantize_weights_sign")
+                  _nbytes(workspace), _stream(W, stream)), "bitlinear_quantize_weights_sign")
 
 
 def bitlinear_forward_sign(Xq, x_scale, W_bits, w_scale, Y, acc=None, stream=None):
-    T, K = Xq.shape
-    N = W_bits.shape[0]
+    T, N, K = _check_proj(Xq, x_scale, W_bits, w_scale, Y, acc, codes_per_byte=8)
     _check(_c_fws(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_bits), _ptr(w_scale), N, _ptr(Y),
                   _ptr(acc), _stream(Xq, stream)), "bitlinear_forward_sign")
 
@@ -260,23 +375,22 @@ def _proj_array(entries):
 
 def bitlinear_forward_sign_grouped(entries, T, stream=None):
     """entries: list of (Xq, x_scale, W_bits, w_scale, Y, acc_or_None)."""
+    _check_entries(entries, T, codes_per_byte=8)
     _check(_c_fwsg(_proj_array(entries), len(entries), T, _stream(entries[0][0], stream)),
            "bitlinear_forward_sign_grouped")
 
 
 def bitlinear_quantize_weights_scale_groups(W, G, W_packed, w_scale, w_gamma, workspace,
                                             stream=None):
-    N, K = W.shape
+    N, K = _check_weights(W, W_packed, 4, (w_scale, int(G)), "w_scale", w_gamma, workspace)
     _check(_c_qwsg(_ptr(W), N, K, int(G), _ptr(W_packed), _ptr(w_scale), _ptr(w_gamma),
-                   _ptr(workspace),
-                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                   _stream(W, stream)), "bitlinear_quantize_weights_scale_groups")
+                   _ptr(workspace), _nbytes(workspace), _stream(W, stream)),
+           "bitlinear_quantize_weights_scale_groups")
 
 
 def bitlinear_forward_scale_groups(Xq, x_scale, W_packed, w_scale, G, Y, acc=None, kernel="auto",
                                    stream=None):
-    T, K = Xq.shape
-    N = W_packed.shape[0]
+    T, N, K = _check_proj(Xq, x_scale, W_packed, w_scale, Y, acc, n_scales=int(G))
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     _check(_c_fwsg_scale(_ptr(Xq), _ptr(x_scale), T, K, _ptr(W_packed), _ptr(w_scale), N, int(G),
                          _ptr(Y), _ptr(acc), k, _stream(Xq, stream)),
@@ -285,6 +399,9 @@ def bitlinear_forward_scale_groups(Xq, x_scale, W_packed, w_scale, G, Y, acc=Non
 
 def bitlinear_forward_grouped_scale_groups(entries, groups, T, stream=None):
     """entries as for bitlinear_forward_grouped; groups[i] = scale groups of entry i."""
+    if len(groups) != len(entries):
+        raise ValueError("one scale-group count per entry: %d for %d" % (len(groups), len(entries)))
+    _check_entries(entries, T, groups=groups)
     g = (_I64 * len(groups))(*[int(x) for x in groups])
     _check(_c_fwg_scale(_proj_array(entries), g, len(entries), T, _stream(entries[0][0], stream)),
            "bitlinear_forward_grouped_scale_groups")
@@ -292,6 +409,10 @@ def bitlinear_forward_grouped_scale_groups(entries, groups, T, stream=None):
 
 class _PreparedScaleGroups:
     def __init__(self, entries, groups, T):
+        if len(groups) != len(entries):
+            raise ValueError("one scale-group count per entry: %d for %d"
+                             % (len(groups), len(entries)))
+        _check_entries(entries, T, groups=groups)
         self._arr = _proj_array(entries)
         self._g = (_I64 * len(groups))(*[int(x) for x in groups])
         self._n, self._T = len(entries), T
@@ -311,35 +432,63 @@ def bitlinear_warmup_lambda(step: int, total: int) -> float:
 
 
 def bitlinear_fake_quant_weights(W, w_scale, lam, W_out, stream=None):
-    N, K = W.shape
+    N, K = _dims(W, "W", 2)
+    _arg(W, "W", _F32)
+    _arg(w_scale, "w_scale", _F32, numel=1)
+    _arg(W_out, "W_out", (_BF16, _I16), shape=(N, K))
+    _same_gpu(W, w_scale, W_out)
     _check(_c_fqw(_ptr(W), N, K, _ptr(w_scale), float(lam), _ptr(W_out), _stream(W, stream)),
            "bitlinear_fake_quant_weights")
 
 
 def bitlinear_fake_quant_acts(X, gain, eps, flags, lam, Xq, x_scale, X_out, x_rinv, stream=None):
-    T, K = X.shape
+    T, K = _dims(X, "X", 2)
+    _arg(X_out, "X_out", (_BF16, _I16), shape=(T, K))
+    _arg(x_rinv, "x_rinv", _F64, numel=T, optional=True)
+    _check_act_entries([(X, gain, Xq, x_scale)], T)
+    _same_gpu(X, X_out, x_rinv)
     _check(_c_fqa(_ptr(X), _ptr(gain), T, K, float(eps), int(flags), float(lam), _ptr(Xq),
                   _ptr(x_scale), _ptr(X_out), _ptr(x_rinv), _stream(X, stream)),
            "bitlinear_fake_quant_acts")
 
 
 def bitlinear_rmsnorm_backward(X, gain, x_rinv, dY, dX, dgain=None, stream=None):
-    T, K = X.shape
+    T, K = _dims(X, "X", 2)
+    _arg(X, "X", _F32)
+    _arg(gain, "gain", _F32, numel=K, optional=True)
+    _arg(x_rinv, "x_rinv", _F64, numel=T)
+    _arg(dY, "dY", _F32, shape=(T, K))
+    _arg(dX, "dX", _F32, shape=(T, K))
+    _arg(dgain, "dgain", _F32, numel=K, optional=True)
+    _same_gpu(X, gain, x_rinv, dY, dX, dgain)
     _check(_c_rbw(_ptr(X), _ptr(gain), _ptr(x_rinv), _ptr(dY), T, K, _ptr(dX), _ptr(dgain),
                   _stream(X, stream)), "bitlinear_rmsnorm_backward")
 
 
 def bitlinear_bitdelta_compress(W_fine, W_base, B, model, D, alpha, workspace, stream=None):
-    N, M = W_fine.shape
+    N, M = _dims(W_fine, "W_fine", 2)
+    _arg(W_fine, "W_fine", _F32)
+    _arg(W_base, "W_base", (_I16, _BF16), shape=(N, M))
+    _arg(D, "D", _U8, shape=(N, M))
+    _arg(alpha, "alpha", _F32, numel=int(B))
+    _arg(workspace, "workspace", _U8)
+    _same_gpu(W_fine, W_base, D, alpha, workspace)
     _check(_c_bdc(_ptr(W_fine), _ptr(W_base), N, M, int(B), int(model), _ptr(D), _ptr(alpha),
-                  _ptr(workspace),
-                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                  _stream(W_fine, stream)), "bitlinear_bitdelta_compress")
+                  _ptr(workspace), _nbytes(workspace), _stream(W_fine, stream)),
+           "bitlinear_bitdelta_compress")
 
 
 def bitlinear_bitdelta_forward(W_base, D, alpha, X, Y, stream=None):
-    N, M = W_base.shape
-    B = X.shape[0]
+    N, M = _dims(W_base, "W_base", 2)
+    B, M2 = _dims(X, "X", 2)
+    if M2 != M:
+        raise ValueError("X has %d features, W_base %d" % (M2, M))
+    _arg(W_base, "W_base", (_I16, _BF16))
+    _arg(D, "D", _U8, shape=(N, M))
+    _arg(alpha, "alpha", _F32, numel=B)
+    _arg(X, "X", _F32)
+    _arg(Y, "Y", _F32, numel=B * N)
+    _same_gpu(W_base, D, alpha, X, Y)
     _check(_c_bdf(_ptr(W_base), _ptr(D), _ptr(alpha), _ptr(X), N, M, int(B), _ptr(Y),
                   _stream(X, stream)), "bitlinear_bitdelta_forward")
 
@@ -358,6 +507,7 @@ class PreparedCall:
 
 
 def prepare_quantize_acts_grouped(entries, T, eps=1e-6, flags=0):
+    _check_act_entries(entries, T)
     arr = (_ActDesc * len(entries))()
     for i, (X, gain, Xq, xs) in enumerate(entries):
         arr[i] = _ActDesc(X.data_ptr(), None if gain is None else gain.data_ptr(), Xq.data_ptr(),
@@ -368,11 +518,8 @@ def prepare_quantize_acts_grouped(entries, T, eps=1e-6, flags=0):
 
 
 def prepare_forward_grouped(entries, T):
-    arr = (_ProjDesc * len(entries))()
-    for i, (Xq, xs, Wp, ws, Y, acc) in enumerate(entries):
-        arr[i] = _ProjDesc(Xq.data_ptr(), xs.data_ptr(), Wp.data_ptr(), ws.data_ptr(),
-                           Y.data_ptr(), None if acc is None else acc.data_ptr(),
-                           Wp.shape[0], Xq.shape[-1])
+    _check_entries(entries, T)
+    arr = _proj_array(entries)
     keep = [t for e in entries for t in e if t is not None]
     # one split-K workspace for the call (its projections run one after another), owned
     # by the prepared call
@@ -385,6 +532,7 @@ def prepare_forward_grouped(entries, T):
 
 
 def prepare_forward_sign_grouped(entries, T):
+    _check_entries(entries, T, codes_per_byte=8)
     keep = [t for e in entries for t in e if t is not None]
     return PreparedCall(_c_fwsg, _proj_array(entries), len(entries), T, (),
                         "bitlinear_forward_sign_grouped", keep)

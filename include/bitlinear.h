@@ -22,7 +22,9 @@
  *     [T tokens, K] row-major, Y = X W^T is [T, N] row-major.
  *   - Every array pointer is a DEVICE pointer owned by the caller; the library keeps
  *     no pointer after the stream-ordered work that uses it has finished, keeps no
- *     device state, and allocates no device memory.
+ *     device state, and allocates no device memory. The one exception is the static
+ *     scratch array of bitlinear_forward_grouped_noalloc (64 MiB per GPU, present
+ *     while the library is loaded; no call allocates or frees it).
  *   - Every compute call is asynchronous on `stream` (NULL = the default stream) and
  *     performs no host synchronization; scales stay on the device.
  *   - Arguments are validated on the host before anything is launched; an invalid call
@@ -221,6 +223,25 @@ bl_status bitlinear_forward_grouped(const bl_proj_desc* descs, int count, int64_
 bl_status bitlinear_forward_grouped_ws(const bl_proj_desc* descs, int count, int64_t T,
                                        void* workspace, size_t workspace_bytes,
                                        bl_stream_t stream);
+
+/* bitlinear_forward_grouped_noalloc: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The same results and kernels as bitlinear_forward_grouped_ws, with the
+ * split-K workspace taken from a library-owned device array of
+ * BL_NOALLOC_SCRATCH_BYTES (64 MiB) instead of an argument. The array is static: each
+ * GPU the library runs on holds its own copy until the process ends, and nothing is
+ * allocated or freed by the call. The caller still owns every input and output.
+ *   - The first call on a device (with that device current) looks up the array's
+ *     address there once; make that first call outside a stream capture.
+ *   - Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ *     (two streams, or two threads) race on it and give undefined results. The array
+ *     needs no clearing: each split writes its partial products before they are read.
+ *   - BL_ERR_WORKSPACE, before any launch, when a projection's split would need more
+ *     than BL_NOALLOC_SCRATCH_BYTES (bitlinear_forward_workspace_bytes); BL_ERR_HIP
+ *     when the address lookup fails (the message names the call). */
+#define BL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bl_status bitlinear_forward_grouped_noalloc(const bl_proj_desc* descs, int count, int64_t T,
+                                            bl_stream_t stream);
 
 /* ---------------------------------------------------------------- weight scale groups
  *

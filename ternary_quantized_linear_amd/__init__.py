@@ -25,6 +25,7 @@ __all__ = [
     "bitlinear_last_hip_error", "bitlinear_abi_version", "quantize_weights",
     "quantize_acts", "forward", "BitLinear", "KERNELS", "NO_NORM", "MAX_K", "MAX_GROUP",
     "prepare_forward_grouped", "prepare_quantize_acts_grouped",
+    "bitlinear_forward_grouped_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +78,8 @@ _c_choice = _sig("bitlinear_forward_choice", [_I64, _I64, _I64])
 _c_fw_wsb = _sig("bitlinear_forward_workspace_bytes", [_I64, _I64, _I64], ctypes.c_size_t)
 _c_fw_ws = _sig("bitlinear_forward_ws", [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_int,
                                          _P, ctypes.c_size_t, _P])
+_c_fwg_na = _sig("bitlinear_forward_grouped_noalloc",
+                 [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
 _c_choice_ws = _sig("bitlinear_forward_choice_ws", [_I64, _I64, _I64, ctypes.c_size_t])
 _c_fwg = _sig("bitlinear_forward_grouped", [ctypes.POINTER(_ProjDesc), ctypes.c_int, _I64, _P])
 _c_fwg_ws = _sig("bitlinear_forward_grouped_ws",
@@ -350,6 +353,18 @@ def bitlinear_forward_grouped_ws(entries, T, workspace, stream=None):
     nb = _nbytes(workspace)
     _check(_c_fwg_ws(_proj_array(entries), len(entries), T, _ptr(workspace), nb,
                      _stream(entries[0][0], stream)), "bitlinear_forward_grouped_ws")
+
+
+def bitlinear_forward_grouped_noalloc(entries, T, stream=None):
+    """bitlinear_forward_grouped_ws with the library's static split-K scratch (64 MiB per
+    GPU) in place of a workspace: nothing is allocated. Calls that overlap on one GPU
+    race on that scratch."""
+    _check_entries(entries, T)
+    _check(_c_fwg_na(_proj_array(entries), len(entries), T, _stream(entries[0][0], stream)),
+           "bitlinear_forward_grouped_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def bitlinear_quantize_weights_sign(W, W_bits, w_scale, w_alpha, workspace, stream=None):

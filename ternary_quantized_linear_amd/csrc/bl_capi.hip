@@ -1,9 +1,12 @@
 // bl_capi.hip -- the C ABI of libbitlinear.so (declared in include/bitlinear.h):
 // host-side argument validation, kernel dispatch, status reporting. No C++ exception
 // crosses the ABI; nothing here allocates device memory or synchronizes the stream
-// (the scratch of split-K products is the caller's workspace).
+// (the scratch of split-K products is the caller's workspace, or for the
+// allocation-free grouped forward a static device array of this file).
 #include <math.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "bl_internal.h"
 
@@ -251,6 +254,67 @@ bl_status bitlinear_forward_grouped_ws(const bl_proj_desc* descs, int count, int
     if (s != BL_OK) return s;
   }
   return BL_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free forward
+// The split-K workspace of bitlinear_forward_grouped_noalloc: a file-scope device array,
+// one copy per GPU, present from the module's load until the process ends. Host code
+// never passes `scratch` itself (in host code it names a host-side stand-in, not the
+// device array): the address comes from hipGetSymbolAddress, once per device, and only
+// that address reaches the kernels.
+static __device__ __align__(256) uint8_t scratch[BL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device, looked up on the first call there.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+bl_status bitlinear_forward_grouped_noalloc(const bl_proj_desc* descs, int count, int64_t T,
+                                            bl_stream_t stream) {
+  if (!descs) return BL_ERR_NULL;
+  if (count < 1 || count > BL_MAX_GROUP) return BL_ERR_ARG;
+  for (int i = 0; i < count; ++i) {
+    const bl_proj_desc& d = descs[i];
+    bl_status s = check_proj(d.Xq, d.x_scale, T, d.K, d.W_packed, d.w_scale, d.N, d.Y, d.acc);
+    if (s != BL_OK) return s;
+    if (bitlinear_forward_workspace_bytes(T, d.N, d.K) > BL_NOALLOC_SCRATCH_BYTES)
+      return BL_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  (void)hipGetLastError();
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) {
+    const bl_status s = hip_status(e);
+    strncat(g_last_error, " (bitlinear_forward_grouped_noalloc: scratch address lookup)",
+            sizeof(g_last_error) - strlen(g_last_error) - 1);
+    return s;
+  }
+  return bitlinear_forward_grouped_ws(descs, count, T, ws, BL_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 bl_status bitlinear_quantize_weights_scale_groups(const float* W, int64_t N, int64_t K, int64_t G,

@@ -73,7 +73,7 @@ typedef enum bl_kernel {
   BL_KERNEL_AUTO = 0,
   BL_KERNEL_GEMV = 1,     /* decode GEMV, int8 dot4; needs T == 1 and K % 64 == 0 */
   BL_KERNEL_SKINNY = 2,   /* skinny int8 MFMA GEMM; needs T <= 128, K % 256 == 0 and
-                             N < 2^24 (passes of 32 tokens) */
+                             N < 2^23 (passes of 64 tokens) */
   BL_KERNEL_PREFILL = 3,  /* LDS-tiled int8 MFMA GEMM; needs K % 128 == 0 */
   BL_KERNEL_GENERIC = 4   /* any K % 4 == 0, any T: one thread per output */
 } bl_kernel;
@@ -374,6 +374,32 @@ bl_status bitlinear_bitdelta_compress(const float* W_fine, const uint16_t* W_bas
 bl_status bitlinear_bitdelta_forward(const uint16_t* W_base, const uint8_t* D, const float* alpha,
                                      const float* X, int64_t N, int64_t M, int B, float* Y,
                                      bl_stream_t stream);
+
+/* ---------------------------------------------------------------- rooflines
+ *
+ * The two rooflines the products are judged by, measured on the part itself
+ * ([HF-1.58] "Tiled matrix multiplication": memory bandwidth and redundant accesses
+ * bound the product, so a decode kernel is compared with a plain read of the same
+ * bytes; the prefill GEMM with the matrix-core rate).
+ *
+ * bitlinear_roof_read: reads `count` (1..BL_MAX_GROUP) device buffers once (bytes[i]
+ * a positive multiple of 16, bases 16-byte aligned), 16 bytes per lane and load, and
+ * writes one word per wave to sink (device, BL_ROOF_READ_SINK_BYTES). schedule 0..3
+ * picks how 1 KiB blocks map to waves (0: grid-stride, one block in flight per wave;
+ * 1: grid-stride, two in flight; 2: a contiguous share per wave, two in flight; 3: as
+ * 0 with no per-block buffer lookup, for one buffer, else as 0); the fastest, timed, is
+ * the read roof of those buffers.
+ *
+ * bitlinear_roof_mfma_i8: `workgroups` workgroups of 4 waves each issue 8 * iters
+ * v_mfma_i32_32x32x32_i8 (65536 int8 ops each) on register operands; sink (device int32,
+ * workgroups * 256 entries) receives a checksum per lane, clocks (device uint64,
+ * workgroups * 16 entries) per wave its start and end shader clock (s_memtime) and
+ * start and end 100 MHz reference clock (s_memrealtime), in that order. */
+#define BL_ROOF_READ_SINK_BYTES ((size_t)65536)
+bl_status bitlinear_roof_read(const void* const* bufs, const int64_t* bytes, int count,
+                              int schedule, uint32_t* sink, bl_stream_t stream);
+bl_status bitlinear_roof_mfma_i8(int iters, int workgroups, int32_t* sink, uint64_t* clocks,
+                                 bl_stream_t stream);
 
 /* ---------------------------------------------------------------- misc */
 const char* bitlinear_status_str(bl_status s);

@@ -26,6 +26,7 @@ __all__ = [
     "quantize_acts", "forward", "BitLinear", "KERNELS", "NO_NORM", "MAX_K", "MAX_GROUP",
     "prepare_forward_grouped", "prepare_quantize_acts_grouped",
     "bitlinear_forward_grouped_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "bitlinear_roof_read", "bitlinear_roof_mfma_i8", "ROOF_READ_SINK_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +106,9 @@ _c_bdc = _sig("bitlinear_bitdelta_compress",
               [_P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P])
 _c_bdf = _sig("bitlinear_bitdelta_forward",
               [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P])
+_c_roof_read = _sig("bitlinear_roof_read",
+                    [ctypes.POINTER(_P), ctypes.POINTER(_I64), ctypes.c_int, ctypes.c_int, _P, _P])
+_c_roof_mfma = _sig("bitlinear_roof_mfma_i8", [ctypes.c_int, ctypes.c_int, _P, _P, _P])
 _c_str = _sig("bitlinear_status_str", [ctypes.c_int], ctypes.c_char_p)
 _c_err = _sig("bitlinear_last_hip_error", [], ctypes.c_char_p)
 _c_ver = _sig("bitlinear_abi_version", [])
@@ -145,8 +149,9 @@ _U8, _I8, _I16, _I32 = torch.uint8, torch.int8, torch.int16, torch.int32
 _F32, _F64, _BF16 = torch.float32, torch.float64, torch.bfloat16
 
 
-def _arg(t, name, dtypes, shape=None, numel=None, optional=False):
-    """Checks one tensor argument (None is allowed only when optional)."""
+def _arg(t, name, dtypes, shape=None, numel=None, optional=False, min_numel=None):
+    """Checks one tensor argument (None is allowed only when optional); numel: exactly
+    that many elements, min_numel: at least that many (a table read by index)."""
     if t is None:
         if optional:
             return
@@ -164,6 +169,9 @@ def _arg(t, name, dtypes, shape=None, numel=None, optional=False):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if numel is not None and t.numel() != int(numel):
         raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), int(numel)))
+    if min_numel is not None and t.numel() < int(min_numel):
+        raise ValueError("%s has %d elements, expected at least %d"
+                         % (name, t.numel(), int(min_numel)))
 
 
 def _dims(t, name, nd):
@@ -201,8 +209,8 @@ def _check_proj(Xq, x_scale, W, w_scale, Y, acc, codes_per_byte=4, n_scales=1, T
         raise ValueError("W_packed has %d bytes per row; K = %d needs %s"
                          % (kb, K, "K / %d" % codes_per_byte))
     _arg(W, "W_packed", _U8)
-    _arg(x_scale, "x_scale", _F32, numel=T0)
-    _arg(w_scale, "w_scale", _F32, numel=n_scales)
+    _arg(x_scale, "x_scale", _F32, min_numel=T0)
+    _arg(w_scale, "w_scale", _F32, min_numel=n_scales)   # scale g read at index g
     _arg(Y, "Y", _F32, numel=T0 * N)
     _arg(acc, "acc", _I32, numel=T0 * N, optional=True)
     _same_gpu(Xq, x_scale, W, w_scale, Y, acc)
@@ -232,7 +240,7 @@ def _check_act_entries(entries, T):
         _arg(X, "X", _F32)
         _arg(gain, "gain", _F32, numel=K, optional=True)
         _arg(Xq, "Xq", _I8, shape=(T, K))
-        _arg(xs, "x_scale", _F32, numel=T)
+        _arg(xs, "x_scale", _F32, min_numel=T)
         _same_gpu(X, gain, Xq, xs)
         dev = X.device if dev is None else dev
         if X.device != dev:
@@ -245,8 +253,8 @@ def _check_weights(W, out, codes_per_byte, scales, scale_name, gamma, workspace)
     if K % codes_per_byte:
         raise ValueError("K = %d is not a multiple of %d" % (K, codes_per_byte))
     _arg(out, "W_packed", _U8, shape=(N, K // codes_per_byte))
-    _arg(scales[0], scale_name, _F32, numel=scales[1])
-    _arg(gamma, "w_gamma", _F64, numel=scales[1], optional=True)
+    _arg(scales[0], scale_name, _F32, min_numel=scales[1])
+    _arg(gamma, "w_gamma", _F64, min_numel=scales[1], optional=True)
     _arg(workspace, "workspace", _U8)
     _same_gpu(W, out, scales[0], gamma, workspace)
     return N, K
@@ -449,7 +457,7 @@ def bitlinear_warmup_lambda(step: int, total: int) -> float:
 def bitlinear_fake_quant_weights(W, w_scale, lam, W_out, stream=None):
     N, K = _dims(W, "W", 2)
     _arg(W, "W", _F32)
-    _arg(w_scale, "w_scale", _F32, numel=1)
+    _arg(w_scale, "w_scale", _F32, min_numel=1)
     _arg(W_out, "W_out", (_BF16, _I16), shape=(N, K))
     _same_gpu(W, w_scale, W_out)
     _check(_c_fqw(_ptr(W), N, K, _ptr(w_scale), float(lam), _ptr(W_out), _stream(W, stream)),
@@ -459,7 +467,7 @@ def bitlinear_fake_quant_weights(W, w_scale, lam, W_out, stream=None):
 def bitlinear_fake_quant_acts(X, gain, eps, flags, lam, Xq, x_scale, X_out, x_rinv, stream=None):
     T, K = _dims(X, "X", 2)
     _arg(X_out, "X_out", (_BF16, _I16), shape=(T, K))
-    _arg(x_rinv, "x_rinv", _F64, numel=T, optional=True)
+    _arg(x_rinv, "x_rinv", _F64, min_numel=T, optional=True)
     _check_act_entries([(X, gain, Xq, x_scale)], T)
     _same_gpu(X, X_out, x_rinv)
     _check(_c_fqa(_ptr(X), _ptr(gain), T, K, float(eps), int(flags), float(lam), _ptr(Xq),
@@ -471,7 +479,7 @@ def bitlinear_rmsnorm_backward(X, gain, x_rinv, dY, dX, dgain=None, stream=None)
     T, K = _dims(X, "X", 2)
     _arg(X, "X", _F32)
     _arg(gain, "gain", _F32, numel=K, optional=True)
-    _arg(x_rinv, "x_rinv", _F64, numel=T)
+    _arg(x_rinv, "x_rinv", _F64, min_numel=T)
     _arg(dY, "dY", _F32, shape=(T, K))
     _arg(dX, "dX", _F32, shape=(T, K))
     _arg(dgain, "dgain", _F32, numel=K, optional=True)
@@ -485,7 +493,7 @@ def bitlinear_bitdelta_compress(W_fine, W_base, B, model, D, alpha, workspace, s
     _arg(W_fine, "W_fine", _F32)
     _arg(W_base, "W_base", (_I16, _BF16), shape=(N, M))
     _arg(D, "D", _U8, shape=(N, M))
-    _arg(alpha, "alpha", _F32, numel=int(B))
+    _arg(alpha, "alpha", _F32, min_numel=int(B))
     _arg(workspace, "workspace", _U8)
     _same_gpu(W_fine, W_base, D, alpha, workspace)
     _check(_c_bdc(_ptr(W_fine), _ptr(W_base), N, M, int(B), int(model), _ptr(D), _ptr(alpha),
@@ -500,12 +508,43 @@ def bitlinear_bitdelta_forward(W_base, D, alpha, X, Y, stream=None):
         raise ValueError("X has %d features, W_base %d" % (M2, M))
     _arg(W_base, "W_base", (_I16, _BF16))
     _arg(D, "D", _U8, shape=(N, M))
-    _arg(alpha, "alpha", _F32, numel=B)
+    _arg(alpha, "alpha", _F32, min_numel=B)
     _arg(X, "X", _F32)
     _arg(Y, "Y", _F32, numel=B * N)
     _same_gpu(W_base, D, alpha, X, Y)
     _check(_c_bdf(_ptr(W_base), _ptr(D), _ptr(alpha), _ptr(X), N, M, int(B), _ptr(Y),
                   _stream(X, stream)), "bitlinear_bitdelta_forward")
+
+
+ROOF_READ_SINK_BYTES = 65536
+
+
+def bitlinear_roof_read(bufs, sink, schedule=0, stream=None):
+    """Reads every tensor in bufs once (the HBM read roof of those bytes) in block
+    schedule 0..3; sink: a uint8 tensor of ROOF_READ_SINK_BYTES on the same GPU."""
+    if len(bufs) < 1 or len(bufs) > MAX_GROUP:
+        raise ValueError("1..%d buffers, got %d" % (MAX_GROUP, len(bufs)))
+    for i, b in enumerate(bufs):
+        _arg(b, "bufs[%d]" % i, (b.dtype,))
+        if _nbytes(b) % 16:
+            raise ValueError("bufs[%d] holds %d bytes, not a multiple of 16" % (i, _nbytes(b)))
+    _arg(sink, "sink", _U8, numel=ROOF_READ_SINK_BYTES)
+    _same_gpu(*bufs, sink)
+    ptrs = (_P * len(bufs))(*[b.data_ptr() for b in bufs])
+    sizes = (_I64 * len(bufs))(*[_nbytes(b) for b in bufs])
+    _check(_c_roof_read(ptrs, sizes, len(bufs), int(schedule), _ptr(sink), _stream(sink, stream)),
+           "bitlinear_roof_read")
+
+
+def bitlinear_roof_mfma_i8(iters, workgroups, sink, clocks, stream=None):
+    """workgroups x 4 waves, each 8 * iters int8 MFMAs of 65536 ops; sink int32
+    [workgroups * 256], clocks int64 [workgroups * 4, 4] (shader clock start/end,
+    100 MHz clock start/end per wave)."""
+    _arg(sink, "sink", _I32, numel=int(workgroups) * 256)
+    _arg(clocks, "clocks", torch.int64, numel=int(workgroups) * 16)
+    _same_gpu(sink, clocks)
+    _check(_c_roof_mfma(int(iters), int(workgroups), _ptr(sink), _ptr(clocks),
+                        _stream(sink, stream)), "bitlinear_roof_mfma_i8")
 
 
 class PreparedCall:

@@ -20,13 +20,14 @@
 // activations where the sign bit is set, P_i, so that sign . x = 2 P_i - sum x
 // (bit -> all-ones mask by a one-bit signed extract, AND, add). The lane's B values
 // b_i + alpha_i (2 P_i - sum x_i) are summed across the wave with DPP; each wave leaves
-// its B row partials in its own LDS slot and adds one arrival to the row's count, and
-// the wave whose arrival completes the count sums the slots in wave order and stores
-// the row. Every sum is taken in a fixed order, so Y is the same bit for bit from call
-// to call. Weights and bits are buffer loads in a
+// its B row partials in its own LDS slot [row][wave][model]; after the sweep, one
+// barrier, and each thread sums the slots of one (row, model) in wave order and stores
+// it. Every sum is taken in a fixed order, so Y is the same bit for bit from call to
+// call. Weights and bits are buffer loads in a
 // ring three rows deep (rows past N read as zeros without a memory access).
 #include "bl_device.h"
 #include "bl_internal.h"
+#include "bl_plan.h"
 
 namespace bl {
 
@@ -46,11 +47,10 @@ struct BdArgs {
   int N, M, B, S, R, nwg;
 };
 
-// LDS per workgroup: the row partials [R][S][kBdMaxB] and the arrival counts [R].
-__host__ __device__ constexpr size_t bd_lds_bytes(int R, int S) {
-  return (size_t)R * ((size_t)S * kBdMaxB + 1) * sizeof(float);
-}
-constexpr size_t kBdLdsMax = 64 * 1024;
+// LDS per workgroup: the row partials [R][S][kBdMaxB] (bl_plan.h).
+using plan::bd_lds_bytes;
+constexpr size_t kBdLdsMax = plan::kBdLdsMax;
+static_assert(plan::kBdMaxB == kBdMaxB && plan::kBdWaves == kBdWaves, "plan constants");
 
 typedef __amdgpu_buffer_rsrc_t BdRsrc;
 constexpr uint32_t kBdOob = 0x80000000u;
@@ -71,14 +71,9 @@ __device__ __forceinline__ float wave_sum_to_last(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(kBdThreads) void bitdelta_kernel(BdArgs a) {
-  extern __shared__ float bd_lds[];
-  float* sums = bd_lds;                                                 // [R][S][kBdMaxB]
-  int* counts = reinterpret_cast<int*>(bd_lds + a.R * a.S * kBdMaxB);  // [R]
-  for (int i = threadIdx.x; i < a.R; i += kBdThreads) counts[i] = 0;
-  __syncthreads();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= a.S) return;  // no barrier follows
+// One wave's share of the rows: codes [1024 wave, 1024 wave + 1024) of every row of the
+// workgroup; its B partial row sums go to LDS slot [row][wave][model].
+__device__ __forceinline__ void bd_sweep(const BdArgs& a, float* sums, int wave) {
   const int lane = threadIdx.x & (kWave - 1);
   const int k0 = wave * kBdWaveCodes + kBdLaneCodes * lane;
   const bool on = k0 < a.M;
@@ -158,26 +153,12 @@ __global__ __launch_bounds__(kBdThreads) void bitdelta_kernel(BdArgs a) {
       v[i] = b + al[i] * (2.0f * p - xs[i]);
     }
     if (prefetch) load_row(d);
-    const int n = wgl + cr * a.nwg;
 #pragma unroll
     for (int i = 0; i < kBdMaxB; ++i) v[i] = wave_sum_to_last(v[i]);
     if (lane == kWave - 1) {
-      // this wave's partials into its own slot; the count's release orders them before
-      // the arrival, its acquire orders the other waves' slots before the reads below
-      float* row = sums + cr * a.S * kBdMaxB;
+      float* row = sums + (cr * a.S + wave) * kBdMaxB;
 #pragma unroll
-      for (int i = 0; i < kBdMaxB; ++i) row[wave * kBdMaxB + i] = v[i];
-      const int old = __hip_atomic_fetch_add(counts + cr, 1, __ATOMIC_ACQ_REL,
-                                             __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (old == a.S - 1 && n < a.N) {
-#pragma unroll
-        for (int i = 0; i < kBdMaxB; ++i) {
-          if (i >= B) continue;
-          float y = row[i];
-          for (int s = 1; s < a.S; ++s) y += row[s * kBdMaxB + i];
-          a.Y[(int64_t)i * a.N + n] = y;
-        }
-      }
+      for (int i = 0; i < kBdMaxB; ++i) row[i] = v[i];
     }
     ++cr;
   };
@@ -192,22 +173,27 @@ __global__ __launch_bounds__(kBdThreads) void bitdelta_kernel(BdArgs a) {
     if (n + d < a.R) step(d, false);
 }
 
+__global__ __launch_bounds__(kBdThreads) void bitdelta_kernel(BdArgs a) {
+  extern __shared__ float bd_lds[];
+  float* sums = bd_lds;  // [R][S][kBdMaxB]: each wave's partial of each row and model
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave < a.S) bd_sweep(a, sums, wave);  // waves past the codes only wait below
+  // every partial is in LDS: thread (row, model) sums the S slots in wave order
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.R * a.B; idx += kBdThreads) {
+    const int cr = idx / a.B, i = idx - cr * a.B;
+    const int n = blockIdx.x + cr * a.nwg;
+    if (n >= a.N) continue;
+    const float* row = sums + cr * a.S * kBdMaxB + i;
+    float y = row[0];
+    for (int s = 1; s < a.S; ++s) y += row[s * kBdMaxB];
+    a.Y[(int64_t)i * a.N + n] = y;
+  }
+}
+
 }  // namespace bl
 
 using namespace bl;
-
-// Workgroups (returned) and rows per workgroup (*R) for N rows: one resident round
-// (cap), or more when a workgroup's row slots would not fit its LDS; then as few
-// workgroups as give the same number of rows each.
-int bd_plan(int64_t N, int S, int cap, int* R) {
-  const int64_t rmax = (int64_t)(kBdLdsMax / bd_lds_bytes(1, S));
-  int64_t nwg = cap < N ? cap : N;
-  int64_t r = (N + nwg - 1) / nwg;
-  if (r > rmax) r = rmax;
-  nwg = (N + r - 1) / r;
-  *R = (int)((N + nwg - 1) / nwg);
-  return (int)nwg;
-}
 
 bool bl_bitdelta_supports(int64_t N, int64_t M, int B) {
   return N >= 1 && M >= 16 && M % 16 == 0 && M <= kBdWaves * kBdWaveCodes && B >= 1 &&
@@ -229,7 +215,7 @@ hipError_t bl_launch_bitdelta(const uint16_t* base, const uint8_t* D, const floa
   a.M = (int)M;
   a.B = B;
   a.S = (int)((M + kBdWaveCodes - 1) / kBdWaveCodes);
-  a.nwg = bd_plan(N, a.S, cap, &a.R);
+  a.nwg = plan::bd_plan(N, a.S, cap, &a.R);
   const size_t lds = bd_lds_bytes(a.R, a.S);
   if (lds > kBdLdsMax) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bitdelta_kernel, dim3((unsigned)a.nwg), dim3(kBdThreads), lds, stream, a);

@@ -77,19 +77,22 @@ bl_status check_proj(const int8_t* Xq, const float* xs, int64_t T, int64_t K,
 }
 
 bl_kernel choose(int64_t T, int64_t N, int64_t K, size_t ws_bytes = 0) {
-  // one token: dot4 GEMV. Up to 128 tokens the streaming MFMA kernel (passes of 32),
-  // except where the LDS-tiled GEMM measures faster: from 96 tokens on, from 64 when it
-  // can cut K into slices that fill the device (which takes a workspace for the
-  // partials), from 32 when it can and K >= 16384 (the streaming kernel makes many
-  // passes over long rows), or when its 128 x 128 tiles alone give every CU two
-  // workgroups. Beyond 128 tokens the tiled GEMM.
+  // one token: dot4 GEMV. Up to 128 tokens the streaming MFMA kernel (passes of 64),
+  // except where the LDS-tiled GEMM measures faster: from 96 tokens on, beyond 64 (a
+  // second streaming pass) when it can cut K into slices that fill the device (which
+  // takes a workspace for the partials), from 32 when it can and K >= 16384 (the
+  // streaming kernel reloads its activations many times over long rows), or when its
+  // 128 x 128 tiles alone give every CU two workgroups. Beyond 128 tokens the tiled
+  // GEMM. Measured on the 70B shapes: gate (K = 8192) at 33 / 48 / 64 tokens 28 / 31 /
+  // 34 us streaming against 35 / 37 / 40 us split; down (K = 28672) 46 / 53 / 62 us
+  // streaming against 33 / 34 / 36 us split.
   if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
   const bool tiled = bl_prefill_supports((int)T, (int)K);
   if (bl_skinny_supports((int)T, N, (int)K)) {
     const int64_t tiles = ((T + 127) / 128) * ((N + 127) / 128);
     const bool split = tiled && bl_prefill_splits((int)T, (int)N, (int)K) &&
                        ws_bytes >= bl_prefill_scratch_bytes((int)T, (int)N, (int)K);
-    const bool prefer_tiled = tiled && (T >= 96 || (T >= 64 && split) ||
+    const bool prefer_tiled = tiled && (T >= 96 || (T > 64 && split) ||
                                         (T >= 32 && K >= 16384 && split) ||
                                         (T > 32 && tiles >= 512));
     if (!prefer_tiled) return BL_KERNEL_SKINNY;
@@ -507,6 +510,29 @@ bl_status bitlinear_bitdelta_forward(const uint16_t* W_base, const uint8_t* D, c
     return BL_ERR_ALIGN;
   (void)hipGetLastError();
   return hip_status(bl_launch_bitdelta(W_base, D, alpha, X, Y, N, M, B, (hipStream_t)stream));
+}
+
+bl_status bitlinear_roof_read(const void* const* bufs, const int64_t* bytes, int count,
+                              int schedule, uint32_t* sink, bl_stream_t stream) {
+  if (!bufs || !bytes || !sink) return BL_ERR_NULL;
+  if (count < 1 || count > BL_MAX_GROUP || schedule < 0 || schedule > 3) return BL_ERR_ARG;
+  for (int i = 0; i < count; ++i) {
+    if (!bufs[i]) return BL_ERR_NULL;
+    if (bytes[i] <= 0 || bytes[i] % 16) return BL_ERR_DIM;
+    if (!aligned16(bufs[i])) return BL_ERR_ALIGN;
+  }
+  if (!aligned_n(sink, 4)) return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_roof_read(bufs, bytes, count, schedule, sink, (hipStream_t)stream));
+}
+
+bl_status bitlinear_roof_mfma_i8(int iters, int workgroups, int32_t* sink, uint64_t* clocks,
+                                 bl_stream_t stream) {
+  if (!sink || !clocks) return BL_ERR_NULL;
+  if (iters < 1 || workgroups < 1 || workgroups > (1 << 20)) return BL_ERR_DIM;
+  if (!aligned_n(sink, 4) || !aligned_n(clocks, 8)) return BL_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(bl_launch_roof_mfma(iters, workgroups, sink, clocks, (hipStream_t)stream));
 }
 
 const char* bitlinear_status_str(bl_status s) {

@@ -23,7 +23,7 @@
 //   - Workgroups are partitioned among the projections of the launch (for example the
 //     seven of a decoder layer) in proportion to their bytes; inside a partition the rows
 //     are swept grid-stride, so each partition reads one compact window of its matrix at
-//     a time. The grid is one round of resident workgroups. Each wave keeps D row groups
+//     a time. The grid is part of one round of resident workgroups. Each wave keeps D row groups
 //     of weights in flight in a ring of registers; a prefetch past the wave's last row
 //     reads a small L2-resident block instead, so no load sits under a branch and each
 //     step waits for exactly the oldest buffer.
@@ -45,6 +45,7 @@
 // sum of the activations whose code is +1, P, and sum c*x = 2P - sum x.
 #include "bl_device.h"
 #include "bl_internal.h"
+#include "bl_plan.h"
 
 #include <climits>
 
@@ -52,12 +53,17 @@ namespace bl {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;  // 4
-constexpr int kGemvDepth = 3;                      // row groups in flight per wave (2-bit)
+// Row groups in flight per wave, 2-bit form: two in the instance for rows of up to 256
+// chunks (with three quarters of a round of workgroups), three in the instance that
+// also takes longer rows (with half a round; the 70B down projection, 448 chunks per
+// row, measured 5% faster so). The 1-bit rows carry half the bytes: four in flight.
+constexpr int kGemvDepth = 2;
+constexpr int kGemvDepthBig = 3;
 #ifndef BL_GEMV_SIGN_DEPTH
 #define BL_GEMV_SIGN_DEPTH 4
 #endif
 constexpr int kGemvSignDepth = BL_GEMV_SIGN_DEPTH;  // the 1-bit rows carry half the bytes
-constexpr int kGemvMaxC = 512;                     // K <= 32768
+constexpr int kGemvMaxC = plan::kGemvMaxC;         // K <= 32768
 
 struct GemvProj {
   const int8_t* Xq;
@@ -196,7 +202,7 @@ __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, 
 // One projection's partition. L lanes per row, I chunks per lane, S waves per row
 // (S > 1 needs L = 64). Wave `wave` of partition workgroup `wgl` takes segment wave % S
 // of row groups wgl * (4/S) + wave / S + k * stride, k = 0, 1, ...
-template <int L, int I, int S, int FMT>
+template <int L, int I, int S, int FMT, int MAXI>
 __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
                                       unsigned long long* slots) {
   constexpr int RW = kWave / L;        // rows per row group
@@ -251,7 +257,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   // The weight ring goes out before the activations: vector loads complete in issue
   // order, so this way the first row waits for one memory latency, not two in a row.
   // The two scales come through the scalar cache, off the vector counter.
-  constexpr int D = FMT == 0 ? kGemvDepth : kGemvSignDepth;
+  constexpr int D = FMT == 0 ? (MAXI >= 2 ? kGemvDepthBig : kGemvDepth) : kGemvSignDepth;
   uint4 w[D][I];
 #pragma unroll
   for (int d = 0; d < D; ++d) load_w(w[d]);
@@ -377,28 +383,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
     __syncthreads();
   }
   switch (P.cfg) {
-    case 0: sweep<16, 1, 1, FMT>(P, wgl, wave, slots); break;  // C <= 16
-    case 1: sweep<32, 1, 1, FMT>(P, wgl, wave, slots); break;  // C <= 32
-    case 2: sweep<64, 1, 1, FMT>(P, wgl, wave, slots); break;  // C <= 64
-    case 3: sweep<64, 1, 2, FMT>(P, wgl, wave, slots); break;  // C <= 128
-    case 4: sweep<64, 1, 4, FMT>(P, wgl, wave, slots); break;  // C <= 256
+    case 0: sweep<16, 1, 1, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 16
+    case 1: sweep<32, 1, 1, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 32
+    case 2: sweep<64, 1, 1, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 64
+    case 3: sweep<64, 1, 2, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 128
+    case 4: sweep<64, 1, 4, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 256
     default:
-      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT>(P, wgl, wave, slots);  // C <= 512
+      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT, MAXI>(P, wgl, wave, slots);  // C <= 512
       break;
   }
-}
-
-struct GemvCfg {
-  int cfg, S, RW;
-};
-
-GemvCfg gemv_cfg(int C) {
-  if (C <= 16) return {0, 1, 4};
-  if (C <= 32) return {1, 1, 2};
-  if (C <= 64) return {2, 1, 1};
-  if (C <= 128) return {3, 2, 1};
-  if (C <= 256) return {4, 4, 1};
-  return {5, 4, 1};
 }
 
 // Workgroups of one instance the device keeps resident at once (queried once per
@@ -419,99 +412,60 @@ bool bl_gemv_sign_supports(int T, int K) {
   return T == 1 && K % 128 == 0 && K / 128 <= kGemvMaxC;
 }
 
-// Relative cost of a byte streamed by segmented rows (S waves meet per row in LDS and
-// an eighth of a segment's lanes may idle) against a byte of a one-wave row, in 1/16.
-#ifndef BL_GEMV_SEG_COST16
-#define BL_GEMV_SEG_COST16 20
-#endif
-
 namespace {
+// The partition (bl_plan.h, gemv_plan): a round of part of the resident workgroups,
+// shared by the projections in proportion to their bytes (segmented rows weighted
+// 1.25x, the costliest first in dispatch order). Measured on the 8B decode layer in one
+// allocation (q|k|v, o, gate|up, down): three quarters of a round with two row groups in
+// flight per wave beat half a round with three by 4-5% (11.2 against 11.7 us, same box,
+// alternating runs; the 70B gate projection 2% faster); launches with rows of more than
+// 256 chunks keep half a round with three in flight (70B down: 5% faster than the
+// other); the 1-bit form keeps half a round with four in flight (5% faster than a full
+// round). A partition dispatched later gets its first rows later, so in the
+// 2-bit form each partition's cost is raised by the fraction of the total dispatched
+// before it (1.5-3% on the 8B layer; the 1-bit form measured 5% slower with it).
 template <int FMT>
 hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t stream) {
   constexpr int kCodes = FMT == 0 ? 64 : 128;  // codes per 16-byte chunk
-  GemvArgs a{};
-  int64_t total = 0;
-  GemvCfg cfg[BL_GROUP_CAP];
-  int64_t cost[BL_GROUP_CAP];
-  int order[BL_GROUP_CAP];
+  int64_t N[BL_GROUP_CAP], K[BL_GROUP_CAP];
   bool big = false;
   for (int i = 0; i < count; ++i) {
-    cfg[i] = gemv_cfg((int)(p[i].K / kCodes));
-    big = big || cfg[i].cfg == 5;
-    const int64_t bytes = (int64_t)p[i].N * (p[i].K / kCodes) * 16;
-    cost[i] = cfg[i].S > 1 ? bytes * BL_GEMV_SEG_COST16 / 16 : bytes;
-    total += cost[i];
-    order[i] = i;
+    N[i] = p[i].N;
+    K[i] = p[i].K;
+    big = big || plan::gemv_cfg((int)(p[i].K / kCodes)).cfg == 5;
   }
-  // Costliest partitions first: workgroups are dispatched in index order over about a
-  // microsecond, and the partition that needs the most time should not start last.
-  for (int i = 1; i < count; ++i)
-    for (int j = i; j > 0 && cost[order[j]] > cost[order[j - 1]]; --j) {
-      const int t = order[j];
-      order[j] = order[j - 1];
-      order[j - 1] = t;
-    }
-  // One round of workgroups, half as many as stay resident (the combine words take at
-  // most a few KB of LDS); each projection gets workgroups in proportion to its cost, at
-  // least one and never one without a row group. Half the resident count, each wave with
-  // three (2-bit) or four (1-bit) row groups in flight, keeps HBM as busy as a full
-  // round with fewer waves to start and to drain (measured: 3% faster than a full round
-  // on the 8B decode layer, 5% on its 1-bit form, 4-15% on the 70B projections).
-  // A partition dispatched later gets its first rows later (its ring loads queue
-  // behind those of the partitions before it), so in the 2-bit form each partition's
-  // cost is raised by the fraction of the total dispatched before it: later partitions
-  // get more workgroups and fewer rows per wave (measured 1.5-3% on the 8B layer; the
-  // 1-bit form, whose waves spend longer on their activations, measured 5% slower).
-  int64_t wcost[BL_GROUP_CAP], wtotal = 0, before = 0;
+  const plan::GemvPlan pl =
+      plan::gemv_plan(N, K, count, kCodes, gemv_resident<FMT>(big, 4096), FMT == 0,
+                      FMT == 0 && !big ? 3 : 1, FMT == 0 && !big ? 4 : 2);
+  GemvArgs a{};
   for (int o = 0; o < count; ++o) {
-    const int64_t c = cost[order[o]];
-    wcost[o] = FMT == 0 ? c + (int64_t)((double)c * (double)before / (double)total) : c;
-    before += c;
-    wtotal += wcost[o];
-  }
-  const int resident = gemv_resident<FMT>(big, 4096);
-  const int cap = resident / 2;
-  int wgs = 0, slots = 0;
-  for (int o = 0; o < count; ++o) {
-    const int i = order[o];
+    const plan::GemvEntry& e = pl.e[o];
+    const bl_proj_internal& q = p[e.src];
     GemvProj& g = a.p[o];
-    const GemvCfg c = cfg[i];
-    g.Xq = p[i].Xq;
-    g.xs = p[i].x_scale;
-    g.W = reinterpret_cast<const uint4*>(p[i].W);
-    g.ws = p[i].w_scale;
-    g.Y = p[i].Y;
-    g.acc = p[i].acc;
-    g.N = (int)p[i].N;
-    g.C = (int)(p[i].K / kCodes);
-    g.cfg = c.cfg;
-    g.CW = (g.C + c.S - 1) / c.S;
-    g.rpg = p[i].rpg;
-    const int groups = (g.N + c.RW - 1) / c.RW;
-    const int gpw = kGemvWaves / c.S;
-    int64_t n = (wcost[o] * (int64_t)(cap - count) + wtotal - 1) / wtotal;
-    n = n < 1 ? 1 : n;
-    const int64_t most = (groups + gpw - 1) / gpw;
-    n = n > most ? most : n;
-    g.nwg = (int)n;
-    g.wg0 = wgs;
-    a.wg0[o] = wgs;
-    wgs += g.nwg;
-    if (c.S > 1) {  // one word per row group a workgroup visits
-      const int64_t steps = (groups + n * gpw - 1) / (n * gpw);
-      const int words = (int)(steps * gpw);
-      slots = words > slots ? words : slots;
-    }
+    g.Xq = q.Xq;
+    g.xs = q.x_scale;
+    g.W = reinterpret_cast<const uint4*>(q.W);
+    g.ws = q.w_scale;
+    g.Y = q.Y;
+    g.acc = q.acc;
+    g.N = e.N;
+    g.C = e.C;
+    g.cfg = e.c.cfg;
+    g.CW = e.CW;
+    g.rpg = q.rpg;
+    g.nwg = e.nwg;
+    g.wg0 = e.wg0;
+    a.wg0[o] = e.wg0;
   }
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
-  a.slots = slots;
-  const size_t lds = sizeof(unsigned long long) * (size_t)slots;
-  if (big)
-    hipLaunchKernelGGL((gemv_kernel<2, FMT>), dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream,
+  a.slots = pl.slots;
+  const size_t lds = sizeof(unsigned long long) * (size_t)pl.slots;
+  if (pl.big)
+    hipLaunchKernelGGL((gemv_kernel<2, FMT>), dim3((unsigned)pl.wgs), dim3(kGemvThreads), lds, stream,
                        a);
   else
-    hipLaunchKernelGGL((gemv_kernel<1, FMT>), dim3((unsigned)wgs), dim3(kGemvThreads), lds, stream,
+    hipLaunchKernelGGL((gemv_kernel<1, FMT>), dim3((unsigned)pl.wgs), dim3(kGemvThreads), lds, stream,
                        a);
   return hipGetLastError();
 }

@@ -78,3 +78,10 @@ hipError_t bl_launch_quantize_weights_sign(const float* W, int64_t N, int64_t K,
 bool bl_gemv_sign_supports(int T, int K);
 hipError_t bl_launch_gemv_sign(const bl_proj_internal* p, int count, hipStream_t stream);
 hipError_t bl_launch_generic_sign(const bl_proj_internal* p, int T, hipStream_t stream);
+
+// Measurement: the HBM read stream and the int8 MFMA stream (bl_roof.hip).
+size_t bl_roof_read_sink_words(int64_t total_bytes);
+hipError_t bl_launch_roof_read(const void* const* bufs, const int64_t* bytes, int count,
+                               int schedule, uint32_t* sink, hipStream_t stream);
+hipError_t bl_launch_roof_mfma(int iters, int wgs, int32_t* sink, uint64_t* clocks,
+                               hipStream_t stream);

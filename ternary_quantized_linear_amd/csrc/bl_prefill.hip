@@ -32,6 +32,7 @@
 // before its stores.
 #include "bl_device.h"
 #include "bl_internal.h"
+#include "bl_plan.h"
 
 namespace bl {
 
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
 
   // XCD-major numbering: workgroup b runs on XCD b % 8
   const int bid = (int)blockIdx.x;
-  const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
+  const int tile = plan::xcd_tile(bid, a.per_xcd);
   if (tile >= a.tiles_m * a.tiles_n) return;
   const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
   __shared__ __attribute__((aligned(16))) int xsum[BM];
 
   const int bid = (int)blockIdx.x;
-  const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
+  const int tile = plan::xcd_tile(bid, a.per_xcd);
   const int mn = a.tiles_m * a.tiles_n;
   if (tile >= mn * a.P) return;
   const int sl = tile / mn, tmn = tile - sl * mn;  // K slice; tiles of one slice adjacent
@@ -544,12 +545,11 @@ hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* 
   a.rpg = p->rpg;
   a.tiles_m = (T + BM - 1) / BM;
   a.tiles_n = (p->N + BN - 1) / BN;
-  const int nkt = p->K / kPfKT;
-  a.ktn = (nkt + P - 1) / P;
-  a.P = (nkt + a.ktn - 1) / a.ktn;  // no empty slice
+  const plan::SplitK sk = plan::splitk_shape(p->K, P);  // no empty slice
+  a.ktn = sk.ktn;
+  a.P = sk.P;
   a.part = a.P > 1 ? part : nullptr;
-  const int tiles = a.tiles_m * a.tiles_n * a.P;
-  a.per_xcd = (tiles + 7) / 8;
+  a.per_xcd = plan::xcd_per((int64_t)a.tiles_m * a.tiles_n * a.P);
   hipLaunchKernelGGL((prefill_big_kernel<MI, NI, WY, OCC>), dim3((unsigned)(8 * a.per_xcd)),
                      dim3(kPfThreads), 0, stream, a);
   if (a.P > 1)
@@ -558,20 +558,8 @@ hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* 
   return hipGetLastError();
 }
 
-// Split-K plan for a product of T <= 128 tokens on 32*MI x 256 tiles: the number of K
-// slices that gives every CU about one workgroup, keeping at least 8 k-tiles per slice;
-// 1 when the tiles alone fill the device.
-inline int splitk_slices(int T, int N, int K) {
-  if (T > 128 || K % kPfKT) return 1;
-  const int MI = (T + 31) / 32;
-  const int64_t tiles = (int64_t)((T + 32 * MI - 1) / (32 * MI)) * ((N + 255) / 256);
-  const int cus = pf_cus();
-  if (tiles >= cus) return 1;
-  int P = (int)((cus + tiles - 1) / tiles);
-  const int most = (K / kPfKT) / 8;
-  P = P < most ? P : most;
-  return P < 1 ? 1 : P;
-}
+// Split-K plan (bl_plan.h) on this device's compute units.
+inline int splitk_slices(int T, int N, int K) { return plan::splitk_slices(T, N, K, pf_cus()); }
 
 template <int BM, int BN>
 hipError_t launch_prefill_t(const bl_proj_internal* p, int T, hipStream_t stream) {
@@ -588,8 +576,7 @@ hipError_t launch_prefill_t(const bl_proj_internal* p, int T, hipStream_t stream
   a.rpg = p->rpg;
   a.tiles_m = (T + BM - 1) / BM;
   a.tiles_n = (p->N + BN - 1) / BN;
-  const int tiles = a.tiles_m * a.tiles_n;
-  a.per_xcd = (tiles + 7) / 8;
+  a.per_xcd = plan::xcd_per((int64_t)a.tiles_m * a.tiles_n);
   hipLaunchKernelGGL((prefill_kernel<BM, BN>), dim3((unsigned)(8 * a.per_xcd)), dim3(kPfThreads), 0,
                      stream, a);
   return hipGetLastError();
@@ -607,8 +594,7 @@ bool bl_prefill_splits(int T, int N, int K) {
 }
 
 size_t bl_prefill_scratch_bytes(int T, int N, int K) {
-  const int P = splitk_slices(T, N, K);
-  return P > 1 ? (size_t)P * T * N * sizeof(int32_t) : 0;
+  return plan::splitk_scratch_bytes(T, N, K, pf_cus());
 }
 
 // Up to 128 tokens: 32*MI x 256 tiles (1 x 4 waves of 32*MI x 64), with K cut into

@@ -1,4 +1,4 @@
-// bl_skinny.hip -- ternary x int8 product for a few tokens (up to 32 per pass) on int8 MFMA
+// bl_skinny.hip -- ternary x int8 product for a few tokens (up to 64 per pass) on int8 MFMA
 // (v_mfma_i32_16x16x64_i8), int32 accumulation, fused rescale.
 //
 // [HF-1.58] "Fine-tuning LLMs to 1.58 bits", "Inference optimization and custom
@@ -41,6 +41,7 @@
 // MFMA output: lane l, register r holds row 4*(l/16) + r of the block, token l % 16.
 #include "bl_device.h"
 #include "bl_internal.h"
+#include "bl_plan.h"
 
 #include <climits>
 
@@ -48,14 +49,14 @@ namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kSkWaves = 8;
+// LDS: the partial tiles of a workgroup's row blocks (up to kSkTileKB KiB), then the
+// per-wave weight regroup areas (16 rows of 64 * MPW + 16 bytes, sized for MPW = 7);
+// all of a CU's LDS is one workgroup's (bl_plan.h)
+constexpr int kSkWaves = plan::kSkWaves;
 constexpr int kSkThreads = kSkWaves * kWave;  // 512
-constexpr int kSkTileKB = 96;  // LDS for the partial tiles of a workgroup's row blocks, KiB
-constexpr size_t kSkLdsMax = kSkTileKB * 1024 + 96 * 4 + 32 * 4;
-constexpr int kSkLdsCU = 160 * 1024;  // LDS of one CU, all of it one workgroup's
-// per-wave weight regroup areas: 16 rows of 64 * MPW + 16 bytes, sized for MPW = 7
-constexpr size_t kSkRegroup = (size_t)kSkWaves * 16 * (64 * 7 + 16);
-static_assert(kSkLdsMax + 16 + kSkRegroup <= (size_t)kSkLdsCU, "LDS plan exceeds a CU");
+constexpr size_t kSkLdsMax = plan::kSkLdsMax;
+constexpr int kSkLdsCU = plan::kSkLdsCU;
+constexpr size_t kSkRegroup = plan::kSkRegroup;
 
 struct SkProj {
   const int8_t* Xq;
@@ -371,7 +372,9 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   switch (P.mpw) {
     case 1: sk_sweep<TB, 1, 4>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
     case 2: sk_sweep<TB, 2, 4>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
-    case 4: sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
+    case 4:
+      if constexpr (TB <= 2) sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs, wlds);
+      break;
     default:
       if constexpr (TB == 1) sk_sweep<TB, 7, 2>(P, T, wgl, wave, tiles, counts, facs, wlds);
       break;
@@ -385,31 +388,6 @@ int sk_resident(size_t lds) {
   return bl_resident_wgs((const void*)skinny_kernel<TB>, kSkThreads, lds, 1, &cached);
 }
 
-// Segment length and team shape for K: the largest fraction of wave-steps spent on real
-// codes (segments past K, idle waves and passes that leave waves without a segment
-// count as waste); ties go to the longer segment.
-void sk_plan(int K, int TB, SkProj& s) {
-  const int c = K / 256;
-  const int cand[4] = {7, 4, 2, 1};
-  double best = -1.0;
-  for (int m : cand) {
-    if (TB == 2 && m > 4) continue;
-    const int nseg = (c + m - 1) / m;
-    const int S = nseg < kSkWaves ? nseg : kSkWaves;
-    const int teams = kSkWaves / S;
-    const int npass = (nseg + S - 1) / S;
-    const double e = (double)teams * c / ((double)kSkWaves * m * npass);
-    if (e > best + 1e-9) {
-      best = e;
-      s.mpw = m;
-      s.nseg = nseg;
-      s.S = S;
-      s.teams = teams;
-      s.npass = npass;
-    }
-  }
-}
-
 // The dynamic-LDS limit is raised once per instance (first launch), never inside a
 // stream capture after that.
 template <int TB>
@@ -417,9 +395,18 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)skinny_kernel<TB>, hipFuncAttributeMaxDynamicSharedMemorySize, kSkLdsCU);
   if (attr != hipSuccess) return attr;
-  SkArgs a{};
-  int64_t total = 0;
+  // one workgroup per CU: its registers and, with the regroup areas, its LDS bound it
+  const int cap = sk_resident<TB>(kSkLdsMax + 16 + kSkRegroup);
+  int64_t N[BL_GROUP_CAP], K[BL_GROUP_CAP];
   for (int i = 0; i < count; ++i) {
+    N[i] = p[i].N;
+    K[i] = p[i].K;
+  }
+  const plan::SkPlan pl = plan::skinny_plan(N, K, count, TB, cap);
+  if (!pl.fits) return hipErrorInvalidValue;
+  SkArgs a{};
+  for (int i = 0; i < count; ++i) {
+    const plan::SkEntry& e = pl.e[i];
     SkProj& s = a.p[i];
     s.Xq = p[i].Xq;
     s.xs = p[i].x_scale;
@@ -427,46 +414,26 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
     s.ws = p[i].w_scale;
     s.Y = p[i].Y;
     s.acc = p[i].acc;
-    s.N = p[i].N;
-    s.K = p[i].K;
-    s.nrb = (p[i].N + 15) / 16;
+    s.N = e.N;
+    s.K = e.K;
+    s.nrb = e.nrb;
     s.rpg = p[i].rpg;
-    sk_plan(p[i].K, TB, s);
-    total += (int64_t)p[i].N * (p[i].K / 4);
+    s.mpw = e.mpw;
+    s.nseg = e.nseg;
+    s.S = e.S;
+    s.teams = e.teams;
+    s.npass = e.npass;
+    s.R = e.R;
+    s.nwg = e.nwg;
+    s.wg0 = e.wg0;
+    a.wg0[i] = e.wg0;
   }
-  // one workgroup per CU: its registers and, with the regroup areas, its LDS bound it
-  const int cap = sk_resident<TB>(kSkLdsMax + 16 + kSkRegroup);
-  int wgs = 0;
-  size_t lds = 0;
-  for (int i = 0; i < count; ++i) {
-    SkProj& s = a.p[i];
-    const int64_t bytes = (int64_t)p[i].N * (p[i].K / 4);
-    int64_t n = (bytes * (int64_t)(cap - count + 1) + total - 1) / total;
-    n = n < 1 ? 1 : n;
-    // every row block of a team keeps its tile in LDS until it is complete: more
-    // workgroups (beyond one resident round) when the tiles would not fit
-    const int rcap = kSkTileKB / (s.teams * TB);
-    const int64_t need_wg = (s.nrb + (int64_t)s.teams * rcap - 1) / ((int64_t)s.teams * rcap);
-    n = n < need_wg ? need_wg : n;
-    const int64_t most = (s.nrb + s.teams - 1) / s.teams;  // no workgroup without a row block
-    n = n > most ? most : n;
-    // as few workgroups as give the same number of row blocks per team
-    const int64_t jmax = (s.nrb + n * s.teams - 1) / (n * s.teams);
-    n = (s.nrb + jmax * s.teams - 1) / (jmax * s.teams);
-    s.nwg = (int)n;
-    s.R = (int)jmax;
-    s.wg0 = wgs;
-    a.wg0[i] = wgs;
-    wgs += s.nwg;
-    const size_t need = (size_t)s.teams * s.R * (TB * 1024 + 4) + 16 * TB * sizeof(float);
-    lds = need > lds ? need : lds;
-  }
-  if (lds > kSkLdsMax) return hipErrorInvalidValue;
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.T = T;
-  a.wbase = (int)((lds + 15) / 16 * 16);
-  lds = (size_t)a.wbase + kSkRegroup;
+  a.wbase = pl.wbase;
+  const int wgs = pl.wgs;
+  const size_t lds = pl.lds;
   hipLaunchKernelGGL(skinny_kernel<TB>, dim3((unsigned)wgs), dim3(kSkThreads), lds, stream, a);
   return hipGetLastError();
 }
@@ -475,17 +442,17 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
 
 using namespace bl;
 
-// Output offsets of one pass (32 tokens) are 32-bit buffer offsets.
+// Output offsets of one pass (64 tokens) are 32-bit buffer offsets.
 bool bl_skinny_supports(int T, int64_t N, int K) {
-  return T >= 1 && T <= 128 && K % 256 == 0 && N * 32 * 4 < (int64_t(1) << 31);
+  return T >= 1 && T <= 128 && K % 256 == 0 && N * 64 * 4 < (int64_t(1) << 31);
 }
 
-// Up to 32 tokens in one launch; more run as passes over slices of 32 tokens (each pass
-// streams the weights again: the choice of the caller when the GEMM's tiles would
-// leave most of the device idle).
+// Up to 64 tokens in one launch (one, two or four token blocks of 16); more run as passes
+// over slices of 64 tokens (each pass streams the weights again: the choice of the
+// caller when the GEMM's tiles would leave most of the device idle).
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
-  for (int t0 = 0; t0 < T; t0 += 32) {
-    const int tn = T - t0 < 32 ? T - t0 : 32;
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    const int tn = T - t0 < 64 ? T - t0 : 64;
     bl_proj_internal q[BL_GROUP_CAP];
     for (int i = 0; i < count; ++i) {
       q[i] = p[i];
@@ -494,8 +461,9 @@ hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStre
       q[i].Y += (int64_t)t0 * p[i].N;
       if (q[i].acc) q[i].acc += (int64_t)t0 * p[i].N;
     }
-    const hipError_t e = tn <= 16 ? launch_skinny_t<1>(q, count, tn, stream)
-                                  : launch_skinny_t<2>(q, count, tn, stream);
+    const hipError_t e = tn <= 16   ? launch_skinny_t<1>(q, count, tn, stream)
+                         : tn <= 32 ? launch_skinny_t<2>(q, count, tn, stream)
+                                    : launch_skinny_t<4>(q, count, tn, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -58,11 +58,11 @@ def test_consistent_cpu_tensors_are_refused_as_off_gpu(bl, calls):
     ("Xq", torch.zeros((2, 64), dtype=torch.uint8), "dtype"),
     ("Xq", torch.zeros((2, 64), dtype=torch.float32), "dtype"),
     ("x_scale", torch.ones(2, dtype=torch.float64), "dtype"),
-    ("x_scale", torch.ones(3), "elements"),
+    ("x_scale", torch.ones(1), "elements"),
     ("W_packed", torch.zeros((8, 15), dtype=torch.uint8), "bytes per row"),
     ("W_packed", torch.zeros((8, 16), dtype=torch.int8), "dtype"),
     ("W_packed", torch.zeros(128, dtype=torch.uint8), "dimensions"),
-    ("w_scale", torch.ones(2), "elements"),
+    ("w_scale", torch.ones(0), "elements"),
     ("Y", torch.empty((2, 7)), "elements"),
     ("Y", torch.empty((2, 8), dtype=torch.float16), "dtype"),
     ("acc", torch.empty((2, 8), dtype=torch.int64), "dtype"),
@@ -162,7 +162,7 @@ def test_weight_quantizer_checks(bl, calls):
     ws = torch.zeros(1024, dtype=torch.uint8)
     for args, msg in [((W, torch.zeros((8, 15), dtype=torch.uint8), b, None, ws), "shape"),
                       ((W.double(), P, b, None, ws), "dtype"),
-                      ((W, P, torch.ones(2), None, ws), "elements"),
+                      ((W, P, torch.ones(0), None, ws), "elements"),
                       ((W, P, b, torch.ones(1), ws), "dtype"),      # gamma must be fp64
                       ((W, P, b, None, None), "required"),
                       ((W, P, b, None, torch.zeros(256, dtype=torch.int32)), "dtype"),
@@ -193,7 +193,7 @@ def test_training_and_bitdelta_checks(bl, calls):
         bl.bitlinear_bitdelta_forward(base, D, torch.ones(2), torch.zeros((2, 32)),
                                       torch.empty((2, 8)))
     with pytest.raises(ValueError, match="elements"):
-        bl.bitlinear_bitdelta_forward(base, D, torch.ones(3), torch.zeros((2, 64)),
+        bl.bitlinear_bitdelta_forward(base, D, torch.ones(1), torch.zeros((2, 64)),
                                       torch.empty((2, 8)))
     with pytest.raises(ValueError, match="shape"):
         bl.bitlinear_bitdelta_compress(torch.zeros((8, 64)), base, 2, 0,

@@ -230,16 +230,18 @@ def test_split_k_workspace_query_and_validation(lib):
     c.argtypes = [I64, I64, I64, ctypes.c_size_t]
     c.restype = ctypes.c_int
     for T, N, K, k in [(31, 8192, 28672, 2), (32, 8192, 28672, 3), (64, 8192, 28672, 3),
-                       (32, 28672, 8192, 2), (64, 28672, 8192, 3), (64, 4096, 4096, 2)]:
-        # from 32 tokens at K >= 16384, from 64 when the slices fill the device (112 row
-        # tiles x 3 slices, 32 x 8); 16 row tiles x 4 slices do not
+                       (32, 28672, 8192, 2), (64, 28672, 8192, 2), (65, 28672, 8192, 3),
+                       (64, 4096, 4096, 2)]:
+        # from 32 tokens at K >= 16384, beyond 64 (a second streaming pass) when the
+        # slices fill the device (112 row tiles x 3 slices, 32 x 8); 16 row tiles x 4
+        # slices do not
         assert c(T, N, K, q(T, N, K)) == k, (T, N, K)
-    need = q(64, 14336, 4096)
-    assert c(64, 14336, 4096, need) == 3 and c(64, 14336, 4096, need - 4) == 2
+    need = q(80, 14336, 4096)
+    assert c(80, 14336, 4096, need) == 3 and c(80, 14336, 4096, need - 4) == 2
     plain = lib.bitlinear_forward_choice
     plain.argtypes = [I64, I64, I64]
     plain.restype = ctypes.c_int
-    assert c(64, 14336, 4096, 0) == plain(64, 14336, 4096) == 2
+    assert c(80, 14336, 4096, 0) == plain(80, 14336, 4096) == 2
     f = lib.bitlinear_forward_ws
     f.argtypes = [P, P, I64, I64, P, P, I64, P, P, ctypes.c_int, P, ctypes.c_size_t, P]
     f.restype = ctypes.c_int

@@ -181,6 +181,10 @@ PRODUCT_CASES = [
     # one and two token blocks, several passes over K, ragged rows
     ("skinny", 12, 45, 512), ("skinny", 20, 45, 512), ("skinny", 16, 77, 28672),
     ("skinny", 7, 19, 4096), ("skinny", 2, 1001, 14336),
+    # four token blocks (33..64 tokens in one pass; segments of 256 and 512 codes),
+    # ragged tokens and rows, several passes over K, and more than one 64-token pass
+    ("skinny", 64, 300, 8192), ("skinny", 48, 1001, 28672), ("skinny", 40, 77, 512),
+    ("skinny", 64, 4097, 14336), ("skinny", 57, 16, 256), ("skinny", 65, 130, 4096),
     ("prefill", 1, 130, 1024), ("prefill", 100, 300, 4096), ("prefill", 129, 129, 1280),
     ("prefill", 263, 520, 14336), ("prefill", 256, 256, 128),
     # large-tile kernels (chosen by tile count): 128 x 256 tiles, then 256 x 256 tiles,

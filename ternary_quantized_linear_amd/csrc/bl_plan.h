@@ -185,33 +185,71 @@ inline void sk_segments(int K, int TB, SkEntry& s) {
   }
 }
 
-// cap: resident workgroups of the skinny kernel (one per CU with its LDS and registers).
-// Workgroups in proportion to each projection's bytes; more when a workgroup's tiles
-// would not fit its LDS; never one without a row block; then as few as give the same
-// number of row blocks per team.
-inline SkPlan skinny_plan(const int64_t* N, const int64_t* K, int count, int TB, int cap) {
+// cap: resident workgroups of the skinny kernel (one per CU with its LDS and registers);
+// T: tokens of the launch. A workgroup of projection i with R row blocks per team reads
+// R * teams * 16 rows of K/4 packed bytes from HBM and the T * K activation bytes of its
+// segments (mostly L2 hits, weighted 1/4 per byte: timelines of the Llama-3-8B layer at
+// T = 16 put the K = 14336 workgroups, with as many activation as weight bytes, ~1.7 us
+// behind the others). The plan takes the smallest per-workgroup cost that one round of
+// at most cap workgroups covers, never a workgroup without a row block, and more
+// workgroups when a workgroup's tiles would not fit its LDS.
+constexpr int64_t kSkActDiv = 4;
+
+struct SkCost {
+  int64_t rowbytes;  // weight bytes of one row block per team
+  int64_t act;       // weighted activation bytes of one workgroup
+  int64_t most;      // workgroups when every team has one row block
+  int64_t need;      // fewest workgroups whose tiles fit the LDS
+};
+
+// Workgroups of entry s at per-workgroup cost tau (0 when tau is below one row block).
+inline int64_t sk_wgs_at(const SkEntry& s, const SkCost& c, int64_t tau) {
+  if (tau < c.act + c.rowbytes) return 0;
+  int64_t r = (tau - c.act) / c.rowbytes;
+  const int64_t rmax = (s.nrb + s.teams - 1) / s.teams;
+  r = r < rmax ? r : rmax;
+  int64_t n = (s.nrb + r * s.teams - 1) / (r * s.teams);
+  return n < c.need ? c.need : n;
+}
+
+inline SkPlan skinny_plan(const int64_t* N, const int64_t* K, int count, int TB, int cap, int T) {
   SkPlan p{};
-  int64_t total = 0;
+  SkCost c[kMaxGroup];
+  int64_t lo = 0, hi = 0;
   for (int i = 0; i < count; ++i) {
     SkEntry& s = p.e[i];
     s.N = (int)N[i];
     s.K = (int)K[i];
     s.nrb = (s.N + 15) / 16;
     sk_segments(s.K, TB, s);
-    total += N[i] * (K[i] / 4);
+    c[i].rowbytes = (int64_t)s.teams * 16 * (K[i] / 4);
+    c[i].act = (int64_t)T * K[i] / kSkActDiv;
+    c[i].most = (s.nrb + s.teams - 1) / s.teams;
+    const int rcap = kSkTileKB / (s.teams * TB);
+    c[i].need = (s.nrb + (int64_t)s.teams * rcap - 1) / ((int64_t)s.teams * rcap);
+    const int64_t one = c[i].act + c[i].rowbytes;  // one row block per team
+    const int64_t all = c[i].act + c[i].rowbytes * c[i].most;
+    lo = one > lo ? one : lo;
+    hi = all > hi ? all : hi;
+  }
+  // smallest tau in [lo, hi] whose workgroups fit one round (hi: the fewest workgroups)
+  auto total = [&](int64_t tau) {
+    int64_t t = 0;
+    for (int i = 0; i < count; ++i) t += sk_wgs_at(p.e[i], c[i], tau);
+    return t;
+  };
+  if (total(lo) > cap) {
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (total(mid) <= cap) hi = mid;
+      else lo = mid + 1;
+    }
   }
   int wgs = 0;
   size_t lds = 0;
   for (int i = 0; i < count; ++i) {
     SkEntry& s = p.e[i];
-    const int64_t bytes = N[i] * (K[i] / 4);
-    int64_t n = (bytes * (int64_t)(cap - count + 1) + total - 1) / total;
-    n = n < 1 ? 1 : n;
-    const int rcap = kSkTileKB / (s.teams * TB);
-    const int64_t need_wg = (s.nrb + (int64_t)s.teams * rcap - 1) / ((int64_t)s.teams * rcap);
-    n = n < need_wg ? need_wg : n;
-    const int64_t most = (s.nrb + s.teams - 1) / s.teams;
-    n = n > most ? most : n;
+    int64_t n = sk_wgs_at(s, c[i], lo);
     const int64_t jmax = (s.nrb + n * s.teams - 1) / (n * s.teams);
     n = (s.nrb + jmax * s.teams - 1) / (jmax * s.teams);
     s.nwg = (int)n;

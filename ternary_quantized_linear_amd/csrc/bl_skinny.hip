@@ -34,10 +34,12 @@
 //   - The S partial 16x16 tiles of a row block meet in LDS by ds_add (integer, so the
 //     order of arrival does not matter), followed by one arrival count per wave; the
 //     wave whose arrival completes the count reads the tile back and stores
-//     Y = fp32(acc) * fp32(beta / s_t). No barrier after the start: every row block has
-//     its own tile for the whole launch (more workgroups when they would not fit).
-//   - Workgroups are partitioned among the projections of a grouped call in proportion
-//     to their bytes, normally one round of resident workgroups.
+//     Y = fp32(acc) * fp32(beta / s_t). One barrier per launch (after the tiles are
+//     zeroed): every row block has its own tile for the whole launch (more workgroups
+//     when they would not fit).
+//   - Workgroups are partitioned among the projections of a grouped call so that each
+//     workgroup's packed-weight bytes plus a quarter of its activation bytes are about
+//     equal, in one round of resident workgroups.
 // MFMA output: lane l, register r holds row 4*(l/16) + r of the block, token l % 16.
 #include "bl_device.h"
 #include "bl_internal.h"
@@ -125,9 +127,14 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
+// Zeroes the partial tiles and arrival counts of a workgroup (every thread takes a share).
+__device__ __forceinline__ void sk_clear(int* lds, int words) {
+  for (int i = threadIdx.x; i < words; i += kSkThreads) lds[i] = 0;
+}
+
 template <int TB, int MPW, int D>
 __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wave, int* tiles,
-                                         int* counts, const float* facs, uint8_t* wlds) {
+                                         int* counts, float* facs, uint8_t* wlds, int nclear) {
   constexpr int RS = 64 * MPW + 16;  // LDS bytes per row of the wave's regroup area
   constexpr int PPR = 4 * MPW;       // 16-byte pieces per row segment
   const int lane = threadIdx.x & (kWave - 1), li = lane & 15, lg = lane >> 4;
@@ -220,11 +227,36 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
     }
   };
 
-  // activations first (L2-resident), then the weight ring; the activation registers are
-  // rearranged while the weights are still in flight
+  // Set-up: the partial tiles zeroed and the rescale factors fac[t] = beta / s_t stored in
+  // LDS, then the workgroup's one barrier, which must come before the first tile add.
+  // With one token block the factors' operands, the activations (L2-resident) and the
+  // weight ring are asked for first and the set-up runs while they are in flight; the
+  // barrier then sits in the first step, so no wave waits for another's loads before
+  // its first MFMAs (the 8B layer at 16 tokens 0.2-0.4 us faster). With more token
+  // blocks each wave asks for up to 40 KB at once, and the barrier goes first (tying
+  // the waves together at their first step measured 2-3% slower at 48-64 tokens). The
+  // activation registers are rearranged while the weights are still in flight.
+  typedef const float __attribute__((address_space(4)))* ConstF;
+  const bool fl = threadIdx.x < 16 * TB;
+  bool synced = TB > 1;
+  if constexpr (TB > 1) {
+    sk_clear(tiles, nclear);
+    if (fl) facs[threadIdx.x] = *(ConstF)P.ws / P.xs[min((int)threadIdx.x, T - 1)];
+    __syncthreads();
+  }
+  float fx = 1.0f;
+  if constexpr (TB == 1) {
+    if (fl) fx = P.xs[min((int)threadIdx.x, T - 1)];
+    __builtin_amdgcn_sched_barrier(0);  // that load first, then the activations and ring
+  }
   issue_B(0);
 #pragma unroll
   for (int d = 0; d < D; ++d) load_w(d);
+  if constexpr (TB == 1) {
+    __builtin_amdgcn_sched_barrier(0);
+    sk_clear(tiles, nclear);
+    if (fl) facs[threadIdx.x] = *(ConstF)P.ws / fx;
+  }
   finish_B();
 
   // the loaded pieces of ring slot d into the wave's LDS rows, then back in the MFMA
@@ -273,6 +305,10 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
     // faster at 8-16 tokens; with two token blocks it measured slower)
     if constexpr (TB == 1) {
       if (more) regroup((d + 1) % D);
+    }
+    if (!synced) {  // one token block: the first step of every wave (see the set-up)
+      __syncthreads();
+      synced = true;
     }
     // partial tile into LDS, then one arrival; the wave that completes the count owns
     // the sum (every earlier arrival's adds were performed before its count)
@@ -357,27 +393,33 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wgl = wg - P.wg0;
   const int nslot = P.teams * P.R;
+  const int nclear = nslot * (TB * 256 + 1);
   int* tiles = sk_lds;
   int* counts = sk_lds + nslot * TB * 256;
   float* facs = reinterpret_cast<float*>(counts + nslot);
-  for (int i = threadIdx.x; i < nslot * (TB * 256 + 1); i += kSkThreads) sk_lds[i] = 0;
-  if (threadIdx.x < 16 * TB) {
-    typedef const float __attribute__((address_space(4)))* ConstF;
-    const float beta = *(ConstF)P.ws;
-    facs[threadIdx.x] = beta / P.xs[min((int)threadIdx.x, T - 1)];
-  }
-  __syncthreads();
-  if (wave >= P.S * P.teams) return;  // leftover waves: no segment (no barrier follows)
+  // Every wave passes exactly one barrier: in its sweep (in the set-up, or in the first
+  // step with one token block: a working wave has at least one step), or here (leftover
+  // waves without a segment, and segment lengths no plan gives).
   uint8_t* const wlds = reinterpret_cast<uint8_t*>(sk_lds) + a->wbase;
-  switch (P.mpw) {
-    case 1: sk_sweep<TB, 1, 4>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
-    case 2: sk_sweep<TB, 2, 4>(P, T, wgl, wave, tiles, counts, facs, wlds); break;
-    case 4:
-      if constexpr (TB <= 2) sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs, wlds);
-      break;
-    default:
-      if constexpr (TB == 1) sk_sweep<TB, 7, 2>(P, T, wgl, wave, tiles, counts, facs, wlds);
-      break;
+  bool swept = false;
+  if (wave < P.S * P.teams) {
+    swept = true;
+    switch (P.mpw) {
+      case 1: sk_sweep<TB, 1, 4>(P, T, wgl, wave, tiles, counts, facs, wlds, nclear); break;
+      case 2: sk_sweep<TB, 2, 4>(P, T, wgl, wave, tiles, counts, facs, wlds, nclear); break;
+      case 4:
+        if constexpr (TB <= 2) sk_sweep<TB, 4, 3>(P, T, wgl, wave, tiles, counts, facs, wlds, nclear);
+        else swept = false;
+        break;
+      default:
+        if constexpr (TB == 1) sk_sweep<TB, 7, 2>(P, T, wgl, wave, tiles, counts, facs, wlds, nclear);
+        else swept = false;
+        break;
+    }
+  }
+  if (!swept) {
+    sk_clear(sk_lds, nclear);
+    __syncthreads();
   }
 }
 
@@ -402,7 +444,7 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
     N[i] = p[i].N;
     K[i] = p[i].K;
   }
-  const plan::SkPlan pl = plan::skinny_plan(N, K, count, TB, cap);
+  const plan::SkPlan pl = plan::skinny_plan(N, K, count, TB, cap, T);
   if (!pl.fits) return hipErrorInvalidValue;
   SkArgs a{};
   for (int i = 0; i < count; ++i) {

@@ -101,7 +101,7 @@ static void check_gemv(const int64_t* N, const int64_t* K, int count, int codes,
 // p < npass; a segment is 256 * mpw codes of K.
 static void check_skinny(const int64_t* N, const int64_t* K, int count, int TB, int cap, int T) {
   ++g_cases;
-  const SkPlan p = skinny_plan(N, K, count, TB, cap);
+  const SkPlan p = skinny_plan(N, K, count, TB, cap, T);
   int next = 0;
   for (int i = 0; i < count; ++i) {
     const SkEntry& e = p.e[i];
@@ -136,6 +136,15 @@ static void check_skinny(const int64_t* N, const int64_t* K, int count, int TB, 
     CHECK((int64_t)16 * (K[i] / 4) < (int64_t(1) << 31), "weight range");
   }
   CHECK(p.wgs == next, "grid");
+  // one round of resident workgroups unless the tiles' LDS alone asks for more
+  int64_t fewest = 0;
+  for (int i = 0; i < count; ++i) {
+    const SkEntry& e = p.e[i];
+    const int rcap = kSkTileKB / (e.teams * TB);
+    const int64_t need = (e.nrb + (int64_t)e.teams * rcap - 1) / ((int64_t)e.teams * rcap);
+    fewest += need > 1 ? need : 1;
+  }
+  if (fewest <= cap) CHECK(p.wgs <= cap, "grid %d exceeds %d resident workgroups", p.wgs, cap);
   if (p.fits) {
     CHECK(p.tile_lds <= kSkLdsMax, "tile LDS %zu", p.tile_lds);
     CHECK(p.lds <= (size_t)kSkLdsCU, "LDS %zu exceeds a CU", p.lds);
@@ -230,7 +239,8 @@ int main() {
   for (int cap : caps)
     for (int TB = 1; TB <= 4; TB *= 2)
       for (int64_t n : rows)
-        for (int64_t k : sks) check_skinny(&n, &k, 1, TB, cap, 16 * TB);
+        for (int64_t k : sks)
+          for (int T : {8 * TB + 1, 16 * TB}) check_skinny(&n, &k, 1, TB, cap, T);
   {
     const int64_t N7[] = {4096, 1024, 1024, 4096, 14336, 14336, 4096};
     const int64_t K7[] = {4096, 4096, 4096, 4096, 4096, 4096, 14336};
@@ -239,11 +249,12 @@ int main() {
     const int64_t Nm[] = {1, 16, 17, 1000, 28672, 3, 65535, 8192};
     const int64_t Km[] = {256, 131840, 512, 14336, 8192, 28672, 256, 28672};
     for (int cap : caps)
-      for (int TB = 1; TB <= 4; TB *= 2) {
-        check_skinny(N7, K7, 7, TB, cap, 16 * TB);
-        check_skinny(N4, K4, 4, TB, cap, 16 * TB);
-        check_skinny(Nm, Km, 8, TB, cap, 16 * TB);
-      }
+      for (int TB = 1; TB <= 4; TB *= 2)
+        for (int T : {8 * TB + 1, 16 * TB}) {
+          check_skinny(N7, K7, 7, TB, cap, T);
+          check_skinny(N4, K4, 4, TB, cap, T);
+          check_skinny(Nm, Km, 8, TB, cap, T);
+        }
   }
   // split K and the XCD-major tile numbering
   const int cuss[] = {256, 304, 80};

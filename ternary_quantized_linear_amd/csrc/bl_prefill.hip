@@ -256,19 +256,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
 //     sum_k x u = acc + sum_k x; the per-token sums sum_k x come from the activation
 //     bytes as they are staged (one v_dot4 per dword) and are subtracted in the
 //     epilogue. All of it is exact integer arithmetic.
-//   - Two LDS stages and two register sets: during the MFMAs of k-tile kt, k-tile kt + 2
-//     is loaded into one register set while k-tile kt + 1 (loaded during kt - 1) is
-//     staged from the other into the other LDS stage, both spread over the MFMA steps;
-//     one barrier per k-tile.
+//   - Two LDS stages and a ring of RD register sets: during the MFMAs of k-tile kt,
+//     k-tile kt + 1 is staged from its register set into the other LDS stage and the
+//     set is refilled at once with k-tile kt + 1 + RD, in three parts spread over the
+//     MFMA steps; one barrier per k-tile. A load so has RD k-tiles to arrive (a second
+//     set that is loaded while the first is staged would give it one): the big tiles
+//     take RD = 2, the few-token tiles, with one workgroup per CU and little work per
+//     k-tile, a deeper ring.
 //   - Split K (a.P > 1): workgroup tile and slice come from one index (the tiles of a
 //     slice adjacent, so an XCD's workgroups share activation k-tiles); the slice's
 //     exact partial (token sums already subtracted) goes to plane p of a.part, and
 //     splitk_reduce_kernel sums the planes and rescales.
 //
-// Packed LDS row of a k-tile: the eight dwords d0..d7 of the row's 32 bytes (dword d =
-// codes 16d..16d+15) stored as d0 d2 d4 d6 | d1 d3 d5 d7, so that lane half lg reads its
-// four MFMA steps (codes 32s + 16lg .. +15, s = 0..3) in one 128-bit read.
-template <int MI, int NI, int WY, int OCC>
+// Order of the codes: the 128 codes of a k-tile are the eight packed dwords d0..d7 of a
+// row (dword d = codes 16d..16d+15). MFMA step s (s = 0..3) takes dword 4 lg + s in lane
+// half lg (the sum over k does not depend on which codes a step takes, as long as both
+// operands take the same ones), so the packed row is staged in LDS as it is in memory
+// and lane half lg reads its four steps in one 128-bit read; the activations of step s
+// in half lg are 16-byte group 4 lg + s of the staged token row.
+template <int MI, int NI, int WY, int OCC, int RD>
 __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) {
   constexpr int WX = 4 / WY;
   constexpr int WM = 32 * MI, WN = 32 * NI, BM = WM * WY, BN = WN * WX;
@@ -313,15 +319,15 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 #pragma unroll
   for (int r = 0; r < WQ; ++r)
     wsrc[r] = a.W + (int64_t)min(n0 + wt + 128 * r, a.N - 1) * Kb + 16 * wh;
-  const int wdst = XB + wt * 32 + 8 * wh;  // + 128 r rows = + 4096 r bytes
+  const int wdst = XB + wt * 32 + 16 * wh;  // + 128 r rows = + 4096 r bytes
 
-  // Two register sets for staging: the loads of k-tile kt + 2 go to one while k-tile
-  // kt + 1, loaded during the previous k-tile, is staged from the other. Items 0..XQ-1
-  // are activation pieces, XQ..XQ+WQ-1 packed weight halves; they are issued and staged
-  // in three parts spread over the MFMA steps.
+  // The register ring: k-tile j lives in set j % RD from its load until it is staged.
+  // Items 0..XQ-1 are activation pieces, XQ..XQ+WQ-1 packed weight halves; they are
+  // staged and reloaded in three parts spread over the MFMA steps.
   constexpr int NITEM = XQ + WQ;
+  static_assert(RD >= 2, "ring depth");
   struct Regs { uint4 v[NITEM]; };
-  Regs ra, rb;
+  Regs ring[RD];
   int rs[XQ];  // this thread's part of the token sums sum_k x
 #pragma unroll
   for (int r = 0; r < XQ; ++r) rs[r] = 0;
@@ -349,10 +355,8 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
         transpose16(in, o);
         *reinterpret_cast<uint4*>(st + xdst + 4096 * q) = make_uint4(o[0], o[1], o[2], o[3]);
       } else {
-        const int r = q - XQ;
-        // dwords 4h, 4h+2 go to the even half, 4h+1, 4h+3 to the odd half
-        *reinterpret_cast<uint2*>(st + wdst + 4096 * r) = make_uint2(R.v[q].x, R.v[q].z);
-        *reinterpret_cast<uint2*>(st + wdst + 4096 * r + 16) = make_uint2(R.v[q].y, R.v[q].w);
+        // the packed half as loaded: no register moves between the load and the store
+        *reinterpret_cast<uint4*>(st + wdst + 4096 * (q - XQ)) = R.v[q];
       }
     }
   };
@@ -365,14 +369,14 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // Reads. Activation fragment i at step s: row wm WM + 32 i + li, group 2s + lg; the
+  // Reads. Activation fragment i at step s: row wm WM + 32 i + li, group 4 lg + s; the
   // swizzle term ((row / 2) % 8) reduces to (li / 2) % 8, so the four per-step offsets
   // are per-lane constants and i adds 4096 i.
   const int li = lane & 31, lg = lane >> 5;
   const int sw = (li >> 1) & 7;
   int xo[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) xo[s] = (wm * WM + li) * kPfKT + 16 * ((2 * s + lg) ^ sw);
+  for (int s = 0; s < 4; ++s) xo[s] = (wm * WM + li) * kPfKT + 16 * ((4 * lg + s) ^ sw);
   const int wo = XB + (wn * WN + li) * 32 + 16 * lg;  // + 1024 j
 
   // One MFMA step s reads MI activation fragments and unpacks NI weight dwords. The
@@ -402,9 +406,9 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
   };
   // One k-tile kt from LDS stage kt % 2: step-0 reads, then four MFMA steps; under
-  // them, the loads of k-tile kt + 2 into register set L and the staging of k-tile
-  // kt + 1 from register set S into the other LDS stage, each in three parts.
-  auto compute = [&](int kt, Regs& L, const Regs& S) {
+  // them, k-tile kt + 1 is staged from register set S into the other LDS stage and S is
+  // reloaded with k-tile kt + 1 + RD, part by part.
+  auto compute = [&](int kt, Regs& S) {
     const uint8_t* st = lds + SB * (kt & 1);
     uint8_t* nx = lds + SB * ((kt + 1) & 1);
     const bool count = kt + 1 < nk;  // past the last k-tile: staged, never read or counted
@@ -416,39 +420,49 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 1, a1, b1);
     mfma_step(a0, b0);
-    load_part(L, kt + 2, 0);
+    store_part(S, nx, count, 0);
+    load_part(S, kt + 1 + RD, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 2, a0, b0);
     mfma_step(a1, b1);
-    load_part(L, kt + 2, 1);
-    store_part(S, nx, count, 0);
+    store_part(S, nx, count, 1);
+    load_part(S, kt + 1 + RD, 1);
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 3, a1, b1);
     mfma_step(a0, b0);
-    load_part(L, kt + 2, 2);
-    store_part(S, nx, count, 1);
+    store_part(S, nx, count, 2);
+    load_part(S, kt + 1 + RD, 2);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(a1, b1);
-    store_part(S, nx, count, 2);
   };
 
+  // k-tiles 0..RD - 1 into the ring in order, k-tile 0 staged, its set refilled with
+  // k-tile RD (loads complete in issue order, so each staging waits for its own tile)
 #pragma unroll
-  for (int part = 0; part < 3; ++part) load_part(ra, 0, part);
+  for (int j = 0; j < RD; ++j)
 #pragma unroll
-  for (int part = 0; part < 3; ++part) store_part(ra, lds, true, part);
+    for (int part = 0; part < 3; ++part) load_part(ring[j], j, part);
 #pragma unroll
-  for (int part = 0; part < 3; ++part) load_part(rb, 1, part);
+  for (int part = 0; part < 3; ++part) store_part(ring[0], lds, true, part);
+#pragma unroll
+  for (int part = 0; part < 3; ++part) load_part(ring[0], RD, part);
   __syncthreads();
+  // unrolled by a multiple of RD and 2, so that k-tile kt's set (kt + 1) % RD is static
+  constexpr int U = RD % 2 ? 2 * RD : RD;
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    compute(kt, ra, rb);
-    __syncthreads();
-    compute(kt + 1, rb, ra);
-    __syncthreads();
+  for (; kt + U <= nk; kt += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      compute(kt + u, ring[(u + 1) % RD]);
+      __syncthreads();
+    }
   }
-  if (kt < nk) {
-    compute(kt, ra, rb);
-    __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U - 1; ++u) {
+    if (kt + u < nk) {
+      compute(kt + u, ring[(u + 1) % RD]);
+      __syncthreads();
+    }
   }
   // token sums: the eight lanes of a row segment hold its eight 16-byte groups
 #pragma unroll
@@ -528,7 +542,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(PfArgs a) {
 
 inline int pf_cus() { return bl_device_cus(); }
 
-template <int MI, int NI, int WY, int OCC>
+// Register ring of the few-token (split-K) tiles: one workgroup per CU streams 8 KB of
+// packed weights per k-tile in a fraction of a microsecond, so a load needs several
+// k-tiles to arrive under load.
+#ifndef BL_PF_RING_SMALL
+#define BL_PF_RING_SMALL 6
+#endif
+constexpr int kPfRingSmall = BL_PF_RING_SMALL;
+
+template <int MI, int NI, int WY, int OCC, int RD>
 hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* part,
                               hipStream_t stream) {
   constexpr int BM = 32 * MI * WY, BN = 32 * NI * (4 / WY);
@@ -550,7 +572,7 @@ hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* 
   a.P = sk.P;
   a.part = a.P > 1 ? part : nullptr;
   a.per_xcd = plan::xcd_per((int64_t)a.tiles_m * a.tiles_n * a.P);
-  hipLaunchKernelGGL((prefill_big_kernel<MI, NI, WY, OCC>), dim3((unsigned)(8 * a.per_xcd)),
+  hipLaunchKernelGGL((prefill_big_kernel<MI, NI, WY, OCC, RD>), dim3((unsigned)(8 * a.per_xcd)),
                      dim3(kPfThreads), 0, stream, a);
   if (a.P > 1)
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((a.N + 1023) / 1024), (unsigned)T),
@@ -614,16 +636,23 @@ hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, int32_t* scratch,
     const int MI = (T + 31) / 32;
     const int64_t tiles = (int64_t)((p->N + 255) / 256) * P;
     if (have && tiles * 4 >= (int64_t)cus * 3) {
-      if (MI == 1) return launch_prefill_big<1, 2, 1, 2>(p, T, P, scratch, stream);
-      if (MI == 2) return launch_prefill_big<2, 2, 1, 2>(p, T, P, scratch, stream);
-      if (MI == 3) return launch_prefill_big<3, 2, 1, 2>(p, T, P, scratch, stream);
-      return launch_prefill_big<4, 2, 1, 2>(p, T, P, scratch, stream);
+      if (tiles <= cus) {  // one workgroup per CU: the deep register ring
+        if (MI == 1) return launch_prefill_big<1, 2, 1, 1, kPfRingSmall>(p, T, P, scratch, stream);
+        if (MI == 2) return launch_prefill_big<2, 2, 1, 1, kPfRingSmall>(p, T, P, scratch, stream);
+        if (MI == 3) return launch_prefill_big<3, 2, 1, 1, kPfRingSmall>(p, T, P, scratch, stream);
+        return launch_prefill_big<4, 2, 1, 1, kPfRingSmall>(p, T, P, scratch, stream);
+      }
+      // more workgroups than CUs: two per CU, each with the two-set ring
+      if (MI == 1) return launch_prefill_big<1, 2, 1, 2, 2>(p, T, P, scratch, stream);
+      if (MI == 2) return launch_prefill_big<2, 2, 1, 2, 2>(p, T, P, scratch, stream);
+      if (MI == 3) return launch_prefill_big<3, 2, 1, 2, 2>(p, T, P, scratch, stream);
+      return launch_prefill_big<4, 2, 1, 2, 2>(p, T, P, scratch, stream);
     }
   }
   const int64_t tiles = (int64_t)((T + 127) / 128) * ((p->N + 255) / 256);
   if (T >= 128 && tiles >= cus)
-    return tiles > cus ? launch_prefill_big<4, 2, 1, 2>(p, T, 1, nullptr, stream)
-                       : launch_prefill_big<4, 2, 1, 1>(p, T, 1, nullptr, stream);
+    return tiles > cus ? launch_prefill_big<4, 2, 1, 2, 2>(p, T, 1, nullptr, stream)
+                       : launch_prefill_big<4, 2, 1, 1, 2>(p, T, 1, nullptr, stream);
   const int64_t big = (int64_t)((T + 255) / 256) * ((p->N + 127) / 128);
   if (T >= 256 && big >= 512) return launch_prefill_t<256, 128>(p, T, stream);
   return launch_prefill_t<128, 128>(p, T, stream);

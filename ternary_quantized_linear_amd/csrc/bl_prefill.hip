@@ -544,11 +544,17 @@ inline int pf_cus() { return bl_device_cus(); }
 
 // Register ring of the few-token (split-K) tiles: one workgroup per CU streams 8 KB of
 // packed weights per k-tile in a fraction of a microsecond, so a load needs several
-// k-tiles to arrive under load.
+// k-tiles to arrive under load (70B down at 8-128 tokens: four sets 1-2% faster than
+// six, eight 2-4% slower). At two workgroups per CU deeper rings measured slower (70B
+// gate 3-6% with three or four sets), and the large tiles would spill.
 #ifndef BL_PF_RING_SMALL
-#define BL_PF_RING_SMALL 6
+#define BL_PF_RING_SMALL 4
 #endif
 constexpr int kPfRingSmall = BL_PF_RING_SMALL;
+#ifndef BL_PF_RING_TWO
+#define BL_PF_RING_TWO 2
+#endif
+constexpr int kPfRingTwo = BL_PF_RING_TWO;  // few-token tiles at two workgroups per CU
 
 template <int MI, int NI, int WY, int OCC, int RD>
 hipError_t launch_prefill_big(const bl_proj_internal* p, int T, int P, int32_t* part,
@@ -643,10 +649,10 @@ hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, int32_t* scratch,
         return launch_prefill_big<4, 2, 1, 1, kPfRingSmall>(p, T, P, scratch, stream);
       }
       // more workgroups than CUs: two per CU, each with the two-set ring
-      if (MI == 1) return launch_prefill_big<1, 2, 1, 2, 2>(p, T, P, scratch, stream);
-      if (MI == 2) return launch_prefill_big<2, 2, 1, 2, 2>(p, T, P, scratch, stream);
-      if (MI == 3) return launch_prefill_big<3, 2, 1, 2, 2>(p, T, P, scratch, stream);
-      return launch_prefill_big<4, 2, 1, 2, 2>(p, T, P, scratch, stream);
+      if (MI == 1) return launch_prefill_big<1, 2, 1, 2, kPfRingTwo>(p, T, P, scratch, stream);
+      if (MI == 2) return launch_prefill_big<2, 2, 1, 2, kPfRingTwo>(p, T, P, scratch, stream);
+      if (MI == 3) return launch_prefill_big<3, 2, 1, 2, kPfRingTwo>(p, T, P, scratch, stream);
+      return launch_prefill_big<4, 2, 1, 2, kPfRingTwo>(p, T, P, scratch, stream);
     }
   }
   const int64_t tiles = (int64_t)((T + 127) / 128) * ((p->N + 255) / 256);

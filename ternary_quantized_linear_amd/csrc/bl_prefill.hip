@@ -42,6 +42,13 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int kPfThreads = 256;
 constexpr int kPfKT = 128;  // codes per k-tile = bytes per staged row
 
+typedef __amdgpu_buffer_rsrc_t PfRsrc;
+
+// A raw buffer resource over [base, base + bytes): reads past the range return zeros.
+__device__ __forceinline__ PfRsrc pf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // LDS position of 16-byte group g (0..7) of staged row t: rows are 128 bytes and the
 // group index is XORed with bits 1..3 of the row, so that 16 lanes reading one group
 // of 16 consecutive rows, or writing the eight groups of 2 consecutive rows, hit 16
@@ -306,19 +313,19 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 
   // Staging. Activation piece r of a thread: row tid/8 + 32r, 16-byte group tid%8 (eight
   // lanes read one 128-byte row segment); its LDS slot is pf_pos, whose swizzle term
-  // depends on the row only through (tid/8 / 2) % 8, the same for every r.
+  // depends on the row only through (tid/8 / 2) % 8, the same for every r. Packed
+  // weight half r: row tid/2 + 128r, half tid%2 (dwords 4h..4h+3). Both are buffer loads
+  // through a resource that covers the tile's rows: one 32-bit offset per thread plus a
+  // uniform term per piece and k-tile (64-bit pointers per piece cost the registers
+  // that the MFMA fragments need), and rows past T or N read zeros without a memory
+  // access (they are never stored).
   const int xt = tid >> 3, xg = tid & 7;
-  const int8_t* xsrc[XQ];
-#pragma unroll
-  for (int r = 0; r < XQ; ++r)
-    xsrc[r] = a.Xq + (int64_t)min(m0 + xt + 32 * r, a.T - 1) * a.K + 16 * xg;
+  const PfRsrc xrs = pf_rsrc(a.Xq + (int64_t)m0 * a.K, (uint32_t)min(BM, a.T - m0) * (uint32_t)a.K);
+  const uint32_t xvo = (uint32_t)xt * (uint32_t)a.K + 16u * (uint32_t)xg;  // + 32 r K + 128 kt
   const int xdst = pf_pos(xt, xg);  // + 32 r rows = + 4096 r bytes
-  // Packed weight half r of a thread: row tid/2 + 128r, half tid%2 (dwords 4h..4h+3).
   const int wt = tid >> 1, wh = tid & 1;
-  const uint8_t* wsrc[WQ];
-#pragma unroll
-  for (int r = 0; r < WQ; ++r)
-    wsrc[r] = a.W + (int64_t)min(n0 + wt + 128 * r, a.N - 1) * Kb + 16 * wh;
+  const PfRsrc wrs = pf_rsrc(a.W + (int64_t)n0 * Kb, (uint32_t)min(BN, a.N - n0) * (uint32_t)Kb);
+  const uint32_t wvo = (uint32_t)wt * (uint32_t)Kb + 16u * (uint32_t)wh;   // + 128 r Kb + 32 kt
   const int wdst = XB + wt * 32 + 16 * wh;  // + 128 r rows = + 4096 r bytes
 
   // The register ring: k-tile j lives in set j % RD from its load until it is staged.
@@ -336,8 +343,10 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
 #pragma unroll
     for (int q = 0; q < NITEM; ++q) {
       if (q * 3 / NITEM != part) continue;
-      if (q < XQ) R.v[q] = *reinterpret_cast<const uint4*>(xsrc[q] + kt * kPfKT);
-      else R.v[q] = *reinterpret_cast<const uint4*>(wsrc[q - XQ] + kt * (kPfKT / 4));
+      const uint32_t off = q < XQ ? xvo + (uint32_t)(32 * q) * (uint32_t)a.K + (uint32_t)kt * kPfKT
+                                  : wvo + (uint32_t)(128 * (q - XQ)) * (uint32_t)Kb + (uint32_t)kt * (kPfKT / 4);
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(q < XQ ? xrs : wrs, off, 0, 0);
+      R.v[q] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
     }
   };
   auto store_part = [&](const Regs& R, uint8_t* st, bool count, int part) {
@@ -418,20 +427,27 @@ __global__ __launch_bounds__(kPfThreads, OCC) void prefill_big_kernel(PfArgs a) 
     v4i a0[MI], b0[NI], a1[MI], b1[NI];
     read_step(st, pk, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
+    // in each step: the next step's fragment reads go out before this step's MFMAs
     read_step(st, pk, 1, a1, b1);
     mfma_step(a0, b0);
     store_part(S, nx, count, 0);
     load_part(S, kt + 1 + RD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 2, a0, b0);
     mfma_step(a1, b1);
     store_part(S, nx, count, 1);
     load_part(S, kt + 1 + RD, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_step(st, pk, 3, a1, b1);
     mfma_step(a0, b0);
     store_part(S, nx, count, 2);
     load_part(S, kt + 1 + RD, 2);
+    __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_step(a1, b1);
   };

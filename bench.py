@@ -58,16 +58,17 @@ def parse():
 
 def counted_traffic():
     """HBM bytes per grouped GEMV launch from the committed counter summary (FETCH_SIZE and
-    WRITE_SIZE passes scaled by a copy kernel of known size), or None when the kernel source
-    has changed since the counters were taken."""
+    WRITE_SIZE passes scaled by a copy kernel of known size), or None when the kernel, its
+    launch plan or its build flags have changed since the counters were taken."""
     import hashlib
     rec_path = os.path.join(ROOT, "profiles", "gemv_kernel_decode8b_counters.json")
     try:
         rec = json.load(open(rec_path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-    except (OSError, ValueError, KeyError):
-        return None
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        checks = rec.get("sources") or {rec["source"]: rec.get("source_sha256")}
+        for path, digest in checks.items():
+            if hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest() != digest:
+                return None
+    except (OSError, ValueError, KeyError, AttributeError):
         return None
     return rec.get("traffic_bytes_per_dispatch")
 

@@ -153,20 +153,23 @@ __device__ __forceinline__ int acc1_total(const Acc8& s, int xsum) {
   return 2 * pos - xsum;
 }
 
-// Activations of 1-bit chunk c (128 codes) as 4 x 8 bit planes, and their sum.
-__device__ __forceinline__ void load_act_chunk1(const int8_t* x, int c, bool on,
-                                                uint32_t (&o)[4][8], int& xsum) {
+// The 128 activations of 1-bit chunk c (eight 16-byte loads).
+__device__ __forceinline__ void load_raw1(const int8_t* x, int c, uint4 (&v)[8]) {
   const uint4* src = reinterpret_cast<const uint4*>(x + 128 * c);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) v[d] = src[d];
+}
+
+// Those activations as 4 x 8 bit planes, and their sum.
+__device__ __forceinline__ void planes1(const uint4 (&v)[8], uint32_t (&o)[4][8], int& xsum) {
   uint32_t raw[32];
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
-    uint4 v = src[d];
-    if (!on) v = make_uint4(0u, 0u, 0u, 0u);
-    raw[4 * d] = v.x;
-    raw[4 * d + 1] = v.y;
-    raw[4 * d + 2] = v.z;
-    raw[4 * d + 3] = v.w;
-    xsum += byte_sum(v.x) + byte_sum(v.y) + byte_sum(v.z) + byte_sum(v.w);
+    raw[4 * d] = v[d].x;
+    raw[4 * d + 1] = v[d].y;
+    raw[4 * d + 2] = v[d].z;
+    raw[4 * d + 3] = v[d].w;
+    xsum += byte_sum(v[d].x) + byte_sum(v[d].y) + byte_sum(v[d].z) + byte_sum(v[d].w);
   }
   // packed dword j covers codes 32j..32j+31; plane i byte b = x[32j + 8b + i], which is
   // byte i % 4 of raw dword 8j + 2b + i / 4
@@ -180,6 +183,31 @@ __device__ __forceinline__ void load_act_chunk1(const int8_t* x, int c, bool on,
       const uint32_t hi = __builtin_amdgcn_perm(raw[8 * j + 6 + h], raw[8 * j + 4 + h], sel);
       o[j][i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
+}
+
+// 1-bit planes in LDS, one 128-byte record per chunk: 16-byte piece q of chunk c at
+// 16 (q ^ (c % 8)), so that the lanes of one read (consecutive chunks, the same piece)
+// spread over all banks; the chunk sums follow the records.
+__device__ __forceinline__ void store_planes1(uint8_t* lds, int c, const uint32_t (&o)[4][8]) {
+  const uint32_t* f = &o[0][0];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    *reinterpret_cast<uint4*>(lds + 128 * c + 16 * (q ^ (c & 7))) =
+        make_uint4(f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]);
+}
+
+__device__ __forceinline__ void read_planes1(const uint8_t* lds, int c, bool on,
+                                             uint32_t (&o)[4][8]) {
+  uint32_t* f = &o[0][0];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint4 v = *reinterpret_cast<const uint4*>(lds + 128 * c + 16 * (q ^ (c & 7)));
+    if (!on) v = make_uint4(0u, 0u, 0u, 0u);
+    f[4 * q] = v.x;
+    f[4 * q + 1] = v.y;
+    f[4 * q + 2] = v.z;
+    f[4 * q + 3] = v.w;
+  }
 }
 
 // Activations of chunk c (64 codes): 4 x 16 bytes, transposed, and their sum; zeros when
@@ -202,9 +230,30 @@ __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, 
 // One projection's partition. L lanes per row, I chunks per lane, S waves per row
 // (S > 1 needs L = 64). Wave `wave` of partition workgroup `wgl` takes segment wave % S
 // of row groups wgl * (4/S) + wave / S + k * stride, k = 0, 1, ...
+// 1-bit: builds this thread's chunks' planes (the first from araw, loaded earlier), stores
+// them with their sums in LDS, and waits for the whole workgroup's.
+__device__ __forceinline__ void publish_planes1(const GemvProj& P, uint8_t* plds, int* psum,
+                                                const uint4 (&araw)[8]) {
+  for (int c = threadIdx.x; c < P.C; c += kGemvThreads) {
+    uint4 v[8];
+    if (c == (int)threadIdx.x) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) v[d] = araw[d];
+    } else {
+      load_raw1(P.Xq, c, v);
+    }
+    uint32_t o[4][8];
+    int xs = 0;
+    planes1(v, o, xs);
+    store_planes1(plds, c, o);
+    psum[c] = xs;
+  }
+  __syncthreads();
+}
+
 template <int L, int I, int S, int FMT, int MAXI>
 __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
-                                      unsigned long long* slots) {
+                                      unsigned long long* slots, int plane_base) {
   constexpr int RW = kWave / L;        // rows per row group
   constexpr int GPW = kGemvWaves / S;  // row groups per workgroup step
   const int lane = threadIdx.x & (kWave - 1);
@@ -215,7 +264,20 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   const int ngroups = (P.N + RW - 1) / RW;
   const int stride = P.nwg * GPW;
   const int g0 = wgl * GPW + wave / S;
-  if (g0 >= ngroups) return;
+  // 1-bit: the workgroup builds the bit planes of the row's activations once, in LDS
+  // after the combine words (thread t builds chunk t, t + 256, ...); the first chunk's
+  // activations are asked for before the weight ring, and every wave, with rows or not,
+  // passes the barrier that publishes the planes
+  uint8_t* const plds = reinterpret_cast<uint8_t*>(slots) + plane_base;
+  int* const psum = reinterpret_cast<int*>(plds + 128 * C);
+  uint4 araw[8];
+  if constexpr (FMT == 1) {
+    if ((int)threadIdx.x < C) load_raw1(P.Xq, threadIdx.x, araw);
+  }
+  if (g0 >= ngroups) {
+    if constexpr (FMT == 1) publish_planes1(P, plds, psum, araw);
+    return;
+  }
   const int glast = g0 + ((ngroups - 1 - g0) / stride) * stride;
 
   // lane chunk i is cbase + jl + L*i when that is inside the segment and the row; a
@@ -265,10 +327,15 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   uint4 x[FMT == 0 ? I : 1][4];
   uint32_t x1[FMT == 1 ? I : 1][4][8];
   int xsum = 0;
+  if constexpr (FMT == 1) publish_planes1(P, plds, psum, araw);
 #pragma unroll
   for (int i = 0; i < I; ++i) {
-    if constexpr (FMT == 0) load_act_chunk(P.Xq, ci[i], on[i], x[i], xsum);
-    else load_act_chunk1(P.Xq, ci[i], on[i], x1[i], xsum);
+    if constexpr (FMT == 0) {
+      load_act_chunk(P.Xq, ci[i], on[i], x[i], xsum);
+    } else {
+      read_planes1(plds, ci[i], on[i], x1[i]);
+      xsum += on[i] ? psum[ci[i]] : 0;
+    }
   }
   typedef const float __attribute__((address_space(4)))* ConstF;
   const float xsc = *(ConstF)P.xs;
@@ -382,14 +449,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
     for (int i = threadIdx.x; i < a->slots; i += kGemvThreads) slots[i] = 0ull;
     __syncthreads();
   }
+  const int pb = (8 * a->slots + 15) & ~15;  // 1-bit planes after the combine words
   switch (P.cfg) {
-    case 0: sweep<16, 1, 1, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 16
-    case 1: sweep<32, 1, 1, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 32
-    case 2: sweep<64, 1, 1, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 64
-    case 3: sweep<64, 1, 2, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 128
-    case 4: sweep<64, 1, 4, FMT, MAXI>(P, wgl, wave, slots); break;  // C <= 256
+    case 0: sweep<16, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 16
+    case 1: sweep<32, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 32
+    case 2: sweep<64, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 64
+    case 3: sweep<64, 1, 2, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 128
+    case 4: sweep<64, 1, 4, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 256
     default:
-      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT, MAXI>(P, wgl, wave, slots);  // C <= 512
+      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT, MAXI>(P, wgl, wave, slots, pb);  // C <= 512
       break;
   }
 }
@@ -434,9 +502,27 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     K[i] = p[i].K;
     big = big || plan::gemv_cfg((int)(p[i].K / kCodes)).cfg == 5;
   }
-  const plan::GemvPlan pl =
-      plan::gemv_plan(N, K, count, kCodes, gemv_resident<FMT>(big, 4096), FMT == 0,
-                      FMT == 0 && !big ? 3 : 1, FMT == 0 && !big ? 4 : 2);
+  // 1-bit: the bit planes of the longest row (128 bytes and a sum per chunk) in LDS,
+  // which bounds the workgroups a CU keeps resident
+  int maxC = 0;
+  for (int i = 0; i < count; ++i) maxC = max(maxC, (int)(p[i].K / kCodes));
+  const size_t plane_bytes = FMT == 1 ? (size_t)(128 + 4) * maxC : 0;
+  int resident = gemv_resident<FMT>(big, 4096);
+  if (FMT == 1) {
+    static const hipError_t attr1 = hipFuncSetAttribute(
+        (const void*)gemv_kernel<1, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static const hipError_t attr2 = hipFuncSetAttribute(
+        (const void*)gemv_kernel<2, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr1 != hipSuccess) return attr1;
+    if (attr2 != hipSuccess) return attr2;
+  }
+  plan::GemvPlan pl = plan::gemv_plan(N, K, count, kCodes, resident, FMT == 0,
+                                      FMT == 0 && !big ? 3 : 1, FMT == 0 && !big ? 4 : 2);
+  if (FMT == 1) {  // fewer workgroups when the planes' LDS keeps fewer resident
+    const size_t need = ((sizeof(unsigned long long) * pl.slots + 15) & ~(size_t)15) + plane_bytes;
+    const int cap = bl_device_cus() * max(1, (int)((size_t)160 * 1024 / need));
+    if (cap < resident) pl = plan::gemv_plan(N, K, count, kCodes, cap, false, 1, 2);
+  }
   GemvArgs a{};
   for (int o = 0; o < count; ++o) {
     const plan::GemvEntry& e = pl.e[o];
@@ -460,7 +546,8 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.slots = pl.slots;
-  const size_t lds = sizeof(unsigned long long) * (size_t)pl.slots;
+  size_t lds = sizeof(unsigned long long) * (size_t)pl.slots;
+  if (FMT == 1) lds = ((lds + 15) & ~(size_t)15) + plane_bytes;
   if (pl.big)
     hipLaunchKernelGGL((gemv_kernel<2, FMT>), dim3((unsigned)pl.wgs), dim3(kGemvThreads), lds, stream,
                        a);

@@ -210,6 +210,35 @@ __device__ __forceinline__ void read_planes1(const uint8_t* lds, int c, bool on,
   }
 }
 
+// 2-bit: the workgroup's transposed activations in LDS, one 64-byte record per chunk with
+// piece q of chunk c at 16 (q ^ ((c / 2) % 4)): two records share a 128-byte bank row,
+// so eight consecutive chunks read the same piece from eight distinct bank groups.
+__device__ __forceinline__ void load_raw0(const int8_t* x, int c, uint4 (&v)[4]) {
+  const uint4* src = reinterpret_cast<const uint4*>(x + 64 * c);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) v[d] = src[d];
+}
+
+__device__ __forceinline__ void store_chunk0(uint8_t* lds, int c, const uint4 (&v)[4], int& xsum) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t in[4] = {v[d].x, v[d].y, v[d].z, v[d].w};
+    uint32_t t[4];
+    transpose16(in, t);
+    *reinterpret_cast<uint4*>(lds + 64 * c + 16 * (d ^ ((c >> 1) & 3))) = make_uint4(t[0], t[1], t[2], t[3]);
+    xsum += byte_sum(v[d].x) + byte_sum(v[d].y) + byte_sum(v[d].z) + byte_sum(v[d].w);
+  }
+}
+
+__device__ __forceinline__ void read_chunk0(const uint8_t* lds, int c, bool on, uint4 (&o)[4]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint4 v = *reinterpret_cast<const uint4*>(lds + 64 * c + 16 * (d ^ ((c >> 1) & 3)));
+    if (!on) v = make_uint4(0u, 0u, 0u, 0u);
+    o[d] = v;
+  }
+}
+
 // Activations of chunk c (64 codes): 4 x 16 bytes, transposed, and their sum; zeros when
 // the lane has no chunk.
 __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, uint4 (&o)[4],
@@ -230,22 +259,29 @@ __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, 
 // One projection's partition. L lanes per row, I chunks per lane, S waves per row
 // (S > 1 needs L = 64). Wave `wave` of partition workgroup `wgl` takes segment wave % S
 // of row groups wgl * (4/S) + wave / S + k * stride, k = 0, 1, ...
-// 1-bit: builds this thread's chunks' planes (the first from araw, loaded earlier), stores
-// them with their sums in LDS, and waits for the whole workgroup's.
-__device__ __forceinline__ void publish_planes1(const GemvProj& P, uint8_t* plds, int* psum,
-                                                const uint4 (&araw)[8]) {
+// Builds this thread's chunks' records (the first from araw, loaded earlier): bit planes
+// (1-bit) or transposed bytes (2-bit), with their sums, in LDS; then waits for the whole
+// workgroup's.
+template <int FMT, int NR>
+__device__ __forceinline__ void publish_acts(const GemvProj& P, uint8_t* plds, int* psum,
+                                             const uint4 (&araw)[NR]) {
   for (int c = threadIdx.x; c < P.C; c += kGemvThreads) {
-    uint4 v[8];
+    uint4 v[NR];
     if (c == (int)threadIdx.x) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d) v[d] = araw[d];
+      for (int d = 0; d < NR; ++d) v[d] = araw[d];
     } else {
-      load_raw1(P.Xq, c, v);
+      if constexpr (FMT == 1) load_raw1(P.Xq, c, v);
+      else load_raw0(P.Xq, c, v);
     }
-    uint32_t o[4][8];
     int xs = 0;
-    planes1(v, o, xs);
-    store_planes1(plds, c, o);
+    if constexpr (FMT == 1) {
+      uint32_t o[4][8];
+      planes1(v, o, xs);
+      store_planes1(plds, c, o);
+    } else {
+      store_chunk0(plds, c, v, xs);
+    }
     psum[c] = xs;
   }
   __syncthreads();
@@ -264,18 +300,20 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   const int ngroups = (P.N + RW - 1) / RW;
   const int stride = P.nwg * GPW;
   const int g0 = wgl * GPW + wave / S;
-  // 1-bit: the workgroup builds the bit planes of the row's activations once, in LDS
-  // after the combine words (thread t builds chunk t, t + 256, ...); the first chunk's
-  // activations are asked for before the weight ring, and every wave, with rows or not,
-  // passes the barrier that publishes the planes
+  // The workgroup prepares the row's activations once, in LDS after the combine words
+  // (thread t takes chunk t, t + 256, ...): 1-bit bit planes, 2-bit transposed bytes;
+  // the first chunk's activations are asked for before the weight ring, and every wave,
+  // with rows or not, passes the barrier that publishes them.
+  constexpr int NR = FMT == 1 ? 8 : 4;  // 16-byte pieces per chunk record
   uint8_t* const plds = reinterpret_cast<uint8_t*>(slots) + plane_base;
-  int* const psum = reinterpret_cast<int*>(plds + 128 * C);
-  uint4 araw[8];
-  if constexpr (FMT == 1) {
-    if ((int)threadIdx.x < C) load_raw1(P.Xq, threadIdx.x, araw);
+  int* const psum = reinterpret_cast<int*>(plds + 16 * NR * C);
+  uint4 araw[NR];
+  if ((int)threadIdx.x < C) {
+    if constexpr (FMT == 1) load_raw1(P.Xq, threadIdx.x, araw);
+    else load_raw0(P.Xq, threadIdx.x, araw);
   }
   if (g0 >= ngroups) {
-    if constexpr (FMT == 1) publish_planes1(P, plds, psum, araw);
+    publish_acts<FMT, NR>(P, plds, psum, araw);
     return;
   }
   const int glast = g0 + ((ngroups - 1 - g0) / stride) * stride;
@@ -327,15 +365,12 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   uint4 x[FMT == 0 ? I : 1][4];
   uint32_t x1[FMT == 1 ? I : 1][4][8];
   int xsum = 0;
-  if constexpr (FMT == 1) publish_planes1(P, plds, psum, araw);
+  publish_acts<FMT, NR>(P, plds, psum, araw);
 #pragma unroll
   for (int i = 0; i < I; ++i) {
-    if constexpr (FMT == 0) {
-      load_act_chunk(P.Xq, ci[i], on[i], x[i], xsum);
-    } else {
-      read_planes1(plds, ci[i], on[i], x1[i]);
-      xsum += on[i] ? psum[ci[i]] : 0;
-    }
+    if constexpr (FMT == 0) read_chunk0(plds, ci[i], on[i], x[i]);
+    else read_planes1(plds, ci[i], on[i], x1[i]);
+    xsum += on[i] ? psum[ci[i]] : 0;
   }
   typedef const float __attribute__((address_space(4)))* ConstF;
   const float xsc = *(ConstF)P.xs;
@@ -502,13 +537,13 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     K[i] = p[i].K;
     big = big || plan::gemv_cfg((int)(p[i].K / kCodes)).cfg == 5;
   }
-  // 1-bit: the bit planes of the longest row (128 bytes and a sum per chunk) in LDS,
+  // the prepared activations of the longest row (a record and a sum per chunk) in LDS,
   // which bounds the workgroups a CU keeps resident
   int maxC = 0;
   for (int i = 0; i < count; ++i) maxC = max(maxC, (int)(p[i].K / kCodes));
-  const size_t plane_bytes = FMT == 1 ? (size_t)(128 + 4) * maxC : 0;
+  const size_t plane_bytes = (size_t)(FMT == 1 ? 128 + 4 : 64 + 4) * maxC;
   int resident = gemv_resident<FMT>(big, 4096);
-  if (FMT == 1) {
+  {
     static const hipError_t attr1 = hipFuncSetAttribute(
         (const void*)gemv_kernel<1, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     static const hipError_t attr2 = hipFuncSetAttribute(
@@ -518,10 +553,12 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
   }
   plan::GemvPlan pl = plan::gemv_plan(N, K, count, kCodes, resident, FMT == 0,
                                       FMT == 0 && !big ? 3 : 1, FMT == 0 && !big ? 4 : 2);
-  if (FMT == 1) {  // fewer workgroups when the planes' LDS keeps fewer resident
+  {  // fewer workgroups when the activation records' LDS keeps fewer resident
     const size_t need = ((sizeof(unsigned long long) * pl.slots + 15) & ~(size_t)15) + plane_bytes;
     const int cap = bl_device_cus() * max(1, (int)((size_t)160 * 1024 / need));
-    if (cap < resident) pl = plan::gemv_plan(N, K, count, kCodes, cap, false, 1, 2);
+    if (cap < resident)
+      pl = plan::gemv_plan(N, K, count, kCodes, cap, FMT == 0, FMT == 0 && !big ? 3 : 1,
+                           FMT == 0 && !big ? 4 : 2);
   }
   GemvArgs a{};
   for (int o = 0; o < count; ++o) {
@@ -546,8 +583,7 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.slots = pl.slots;
-  size_t lds = sizeof(unsigned long long) * (size_t)pl.slots;
-  if (FMT == 1) lds = ((lds + 15) & ~(size_t)15) + plane_bytes;
+  const size_t lds = ((sizeof(unsigned long long) * (size_t)pl.slots + 15) & ~(size_t)15) + plane_bytes;
   if (pl.big)
     hipLaunchKernelGGL((gemv_kernel<2, FMT>), dim3((unsigned)pl.wgs), dim3(kGemvThreads), lds, stream,
                        a);

@@ -93,6 +93,12 @@ static void check_gemv(const int64_t* N, const int64_t* K, int count, int codes,
   }
   CHECK(p.wgs == next, "grid %d vs %d", p.wgs, next);
   CHECK((size_t)p.slots * 8 <= 64 * 1024, "combine words %d exceed 64 KiB", p.slots);
+  // the kernel's LDS: the combine words, then one prepared-activation record and a sum
+  // per chunk of the longest row (64 + 4 bytes for 2-bit chunks, 128 + 4 for 1-bit)
+  int64_t maxC = 0;
+  for (int i = 0; i < count; ++i) maxC = K[i] / codes > maxC ? K[i] / codes : maxC;
+  const size_t lds = (((size_t)p.slots * 8 + 15) & ~(size_t)15) + (size_t)(codes + 4) * maxC;
+  CHECK(lds <= 160 * 1024, "GEMV LDS %zu exceeds a CU", lds);
 }
 
 // ---------------------------------------------------------------- skinny

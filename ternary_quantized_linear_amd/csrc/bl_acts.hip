@@ -39,24 +39,31 @@ struct ActArgs {
   float lam;
 };
 
-// Training side ([HF-1.58] "Dynamic warm-up quantization", "How quantization works"):
-// y + lam * (q / s - y) with q / s one fp32 division and every step one fp32 rounding
-// (no contraction), then bf16.
-__device__ __forceinline__ uint32_t fq_one(float y, int q, float s, float lam) {
-  const float xd = (float)q / s;
-  const float d = xd - y;
-  const float t = lam * d;
-  return bf16_bits(y + t);
-}
-
 __device__ __forceinline__ int code_of(float v, float s) {
   return (int)fminf(fmaxf(rintf(v * s), -128.0f), 127.0f);
 }
 
-__device__ __forceinline__ uint2 fq4(float4 y, float s, float lam) {
-  const uint32_t a = fq_one(y.x, code_of(y.x, s), s, lam), b = fq_one(y.y, code_of(y.y, s), s, lam);
-  const uint32_t c = fq_one(y.z, code_of(y.z, s), s, lam), d = fq_one(y.w, code_of(y.w, s), s, lam);
+// Training side ([HF-1.58] "Dynamic warm-up quantization", "How quantization works"):
+// y + lam * (q / s - y) with q / s one fp32 division and every step one fp32 rounding
+// (no contraction), then bf16. q / s is read from a table of the 256 quotients of the
+// row: each entry is that IEEE division, done once per row instead of once per element.
+__device__ __forceinline__ uint32_t fq_tab(float y, float s, float lam, const float* quot) {
+  const float d = quot[code_of(y, s) + 128] - y;
+  const float t = lam * d;
+  return bf16_bits(y + t);
+}
+
+__device__ __forceinline__ uint2 fq4_tab(float4 y, float s, float lam, const float* quot) {
+  const uint32_t a = fq_tab(y.x, s, lam, quot), b = fq_tab(y.y, s, lam, quot);
+  const uint32_t c = fq_tab(y.z, s, lam, quot), d = fq_tab(y.w, s, lam, quot);
   return make_uint2(a | (b << 16), c | (d << 16));
+}
+
+// quot[i] = fp32(i - 128) / s for the 256 codes, by the workgroup's threads; the caller
+// synchronizes before the table is read.
+template <int NT>
+__device__ __forceinline__ void fill_quot(float* quot, float s) {
+  for (int i = threadIdx.x; i < 256; i += NT) quot[i] = (float)(i - 128) / s;
 }
 
 // Block-wide double-double sum. Each wave reduces its lanes with DPP into lane 63; after
@@ -198,11 +205,14 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   }
   if constexpr (FQ) {
     if (e.xfq) {
+      __shared__ float quot[256];
+      fill_quot<NT>(quot, s);
+      __syncthreads();
       uint2* f2 = reinterpret_cast<uint2*>(e.xfq + (int64_t)t * e.K);
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         int i = threadIdx.x + j * NT;
-        if (i < K4) f2[i] = fq4(v[j], s, a.lam);
+        if (i < K4) f2[i] = fq4_tab(v[j], s, a.lam, quot);
       }
     }
   }
@@ -243,11 +253,18 @@ __global__ __launch_bounds__(NT) void act_quant_stream(ActArgs a) {
   m = block_max<NT>(m, sh_m);
   const float s = 127.0f / fmaxf(m, 1e-5f);
   uint32_t* q4 = reinterpret_cast<uint32_t*>(e.Xq + (int64_t)t * e.K);
+  __shared__ float quot[FQ ? 256 : 1];
+  if constexpr (FQ) {
+    if (e.xfq) {
+      fill_quot<NT>(quot, s);
+      __syncthreads();
+    }
+  }
   for (int i = threadIdx.x; i < K4; i += NT) {
     const float4 y = load_y(i);
     q4[i] = quant4(y, s);
     if constexpr (FQ) {
-      if (e.xfq) reinterpret_cast<uint2*>(e.xfq + (int64_t)t * e.K)[i] = fq4(y, s, a.lam);
+      if (e.xfq) reinterpret_cast<uint2*>(e.xfq + (int64_t)t * e.K)[i] = fq4_tab(y, s, a.lam, quot);
     }
   }
   if (threadIdx.x == 0) e.s[t] = s;

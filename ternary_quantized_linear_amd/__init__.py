@@ -430,24 +430,13 @@ def bitlinear_forward_grouped_scale_groups(entries, groups, T, stream=None):
            "bitlinear_forward_grouped_scale_groups")
 
 
-class _PreparedScaleGroups:
-    def __init__(self, entries, groups, T):
-        if len(groups) != len(entries):
-            raise ValueError("one scale-group count per entry: %d for %d"
-                             % (len(groups), len(entries)))
-        _check_entries(entries, T, groups=groups)
-        self._arr = _proj_array(entries)
-        self._g = (_I64 * len(groups))(*[int(x) for x in groups])
-        self._n, self._T = len(entries), T
-        self._keep = [t for e in entries for t in e if t is not None]
-
-    def __call__(self, stream=None):
-        _check(_c_fwg_scale(self._arr, self._g, self._n, self._T, _stream(self._keep[0], stream)),
-               "bitlinear_forward_grouped_scale_groups")
-
-
 def prepare_forward_grouped_scale_groups(entries, groups, T):
-    return _PreparedScaleGroups(entries, groups, T)
+    if len(groups) != len(entries):
+        raise ValueError("one scale-group count per entry: %d for %d" % (len(groups), len(entries)))
+    _check_entries(entries, T, groups=groups)
+    g = (_I64 * len(groups))(*[int(x) for x in groups])
+    return PreparedCall(_c_fwg_scale, _proj_array(entries), len(entries), T, (),
+                        "bitlinear_forward_grouped_scale_groups", _keep(entries), pre=(g,))
 
 
 def bitlinear_warmup_lambda(step: int, total: int) -> float:
@@ -548,16 +537,21 @@ def bitlinear_roof_mfma_i8(iters, workgroups, sink, clocks, stream=None):
 
 
 class PreparedCall:
-    """A grouped ABI call with its descriptor array marshalled once. Calling it
-    launches on the current stream at call time (so it can be captured into a graph)."""
+    """A grouped ABI call with its descriptor array marshalled once:
+    fn(arr, *pre, count, T, *extra, stream). Calling it launches on the current stream at
+    call time (so it can be captured into a graph); keep holds the tensors it points to."""
 
-    def __init__(self, fn, arr, count, T, extra, where, keep):
+    def __init__(self, fn, arr, count, T, extra, where, keep, pre=()):
         self._fn, self._arr, self._count, self._T = fn, arr, count, T
-        self._extra, self._where, self._keep = extra, where, keep
+        self._extra, self._where, self._keep, self._pre = extra, where, keep, pre
 
     def __call__(self, stream=None):
         s = _stream(self._keep[0], stream)
-        _check(self._fn(self._arr, self._count, self._T, *self._extra, s), self._where)
+        _check(self._fn(self._arr, *self._pre, self._count, self._T, *self._extra, s), self._where)
+
+
+def _keep(entries):
+    return [t for e in entries for t in e if t is not None]
 
 
 def prepare_quantize_acts_grouped(entries, T, eps=1e-6, flags=0):
@@ -566,15 +560,14 @@ def prepare_quantize_acts_grouped(entries, T, eps=1e-6, flags=0):
     for i, (X, gain, Xq, xs) in enumerate(entries):
         arr[i] = _ActDesc(X.data_ptr(), None if gain is None else gain.data_ptr(), Xq.data_ptr(),
                           xs.data_ptr(), X.shape[-1])
-    keep = [t for e in entries for t in e if t is not None]
     return PreparedCall(_c_qag, arr, len(entries), T, (ctypes.c_float(eps), ctypes.c_uint32(flags)),
-                        "bitlinear_quantize_acts_grouped", keep)
+                        "bitlinear_quantize_acts_grouped", _keep(entries))
 
 
 def prepare_forward_grouped(entries, T):
     _check_entries(entries, T)
     arr = _proj_array(entries)
-    keep = [t for e in entries for t in e if t is not None]
+    keep = _keep(entries)
     # one split-K workspace for the call (its projections run one after another), owned
     # by the prepared call
     nb = max(_c_fw_wsb(T, Wp.shape[0], Xq.shape[-1]) for (Xq, _, Wp, _, _, _) in entries)
@@ -587,9 +580,8 @@ def prepare_forward_grouped(entries, T):
 
 def prepare_forward_sign_grouped(entries, T):
     _check_entries(entries, T, codes_per_byte=8)
-    keep = [t for e in entries for t in e if t is not None]
     return PreparedCall(_c_fwsg, _proj_array(entries), len(entries), T, (),
-                        "bitlinear_forward_sign_grouped", keep)
+                        "bitlinear_forward_sign_grouped", _keep(entries))
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -96,3 +96,59 @@ def test_scale_groups_end_to_end_and_grouped_call(bl):
     for (_, _, _, _, Yi, ai), ri in zip(entries, refs):
         assert np.array_equal(host(ai), ri["acc"])
         assert_y_close(host(Yi), ri["Y"], "grouped call")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_fused_layer_layout_prepared(bl, T):
+    # The decode layer in one allocation (reading L1): q|k|v and gate|up each quantized
+    # per projection into consecutive rows, one scale per segment (rows per group = gcd
+    # of the parts' rows), launched as one prepared grouped call with per-entry scale
+    # groups. Every output must equal, bit for bit, the separate product of its
+    # projection with its own scale; acc against the oracle.
+    shapes = {"q": (192, 512), "k": (64, 512), "v": (64, 512), "o": (128, 512),
+              "gate": (320, 512), "up": (320, 512), "down": (128, 1280)}
+    fused = (("qkv", ("q", "k", "v"), 0), ("o", ("o",), 1), ("gateup", ("gate", "up"), 0),
+             ("down", ("down",), 2))
+    inputs = [workloads.acts_normal(T, 512, 40 + T), workloads.acts_normal(T, 512, 41 + T),
+              workloads.acts_normal(T, 1280, 42 + T)]
+    acts = [bl.quantize_acts(dev(X)) for X in inputs]
+    total = sum(n * k // 4 for (n, k) in shapes.values())
+    buf = torch.empty(total, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(bl.bitlinear_weight_workspace_bytes(*s) for s in shapes.values()),
+                     dtype=torch.uint8, device=DEV)
+    views, betas, Ws, off = {}, {}, {}, 0
+    for p, (n, k) in shapes.items():
+        Ws[p] = workloads.weights(n, k, 50 + n + k) * np.float32(1.0 + 0.3 * len(p))
+        views[p] = buf[off: off + n * k // 4].view(n, k // 4)
+        betas[p] = torch.empty(1, dtype=torch.float32, device=DEV)
+        bl.bitlinear_quantize_weights(dev(Ws[p]), views[p], betas[p], None, ws)
+        off += n * k // 4
+    entries, groups, outs, base = [], [], [], 0
+    for name, parts, inp in fused:
+        rows = [shapes[p][0] for p in parts]
+        k = shapes[parts[0]][1]
+        rpg = int(np.gcd.reduce(rows))
+        scale = torch.cat([betas[p].repeat(shapes[p][0] // rpg) for p in parts])
+        n = sum(rows)
+        Wf = buf[base: base + n * k // 4].view(n, k // 4)
+        base += n * k // 4
+        Y = torch.empty((T, n), dtype=torch.float32, device=DEV)
+        A = torch.empty((T, n), dtype=torch.int32, device=DEV)
+        entries.append((acts[inp][0], acts[inp][1], Wf, scale, Y, A))
+        groups.append(n // rpg)
+        outs.append((parts, inp, Y, A))
+    call = bl.prepare_forward_grouped_scale_groups(entries, groups, T)
+    call()
+    call()  # a second launch of the same prepared call gives the same bits
+    for parts, inp, Y, A in outs:
+        r0 = 0
+        for p in parts:
+            n, k = shapes[p]
+            Ys = torch.empty((T, n), dtype=torch.float32, device=DEV)
+            As = torch.empty((T, n), dtype=torch.int32, device=DEV)
+            bl.bitlinear_forward(acts[inp][0], acts[inp][1], views[p], betas[p], Ys, As)
+            assert torch.equal(A[:, r0:r0 + n], As), p
+            assert torch.equal(Y[:, r0:r0 + n], Ys), p
+            acc_o = oracle.product(host(acts[inp][0]), host(views[p]), k)
+            assert np.array_equal(host(As), acc_o), p
+            r0 += n

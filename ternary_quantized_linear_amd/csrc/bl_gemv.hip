@@ -54,7 +54,7 @@ namespace bl {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;  // 4
 // Row groups in flight per wave, 2-bit form: two in the instance for rows of up to 256
-// chunks (with three quarters of a round of workgroups), three in the instance that
+// chunks (with five eighths of a round of workgroups), three in the instance that
 // also takes longer rows (with half a round; the 70B down projection, 448 chunks per
 // row, measured 5% faster so). The 1-bit rows carry half the bytes: four in flight.
 constexpr int kGemvDepth = 2;
@@ -521,12 +521,15 @@ namespace {
 // 1.25x, the costliest first in dispatch order). Measured on the 8B decode layer in one
 // allocation (q|k|v, o, gate|up, down): three quarters of a round with two row groups in
 // flight per wave beat half a round with three by 4-5% (11.2 against 11.7 us, same box,
-// alternating runs; the 70B gate projection 2% faster); launches with rows of more than
-// 256 chunks keep half a round with three in flight (70B down: 5% faster than the
-// other); the 1-bit form keeps half a round with four in flight (5% faster than a full
-// round). A partition dispatched later gets its first rows later, so in the
-// 2-bit form each partition's cost is raised by the fraction of the total dispatched
-// before it (1.5-3% on the 8B layer; the 1-bit form measured 5% slower with it).
+// alternating runs; the 70B gate projection 2% faster), and five eighths beat three
+// quarters by 1.4% (11.35 against 11.51 us; 70B gate 12.3-12.45 against 12.6, down the
+// same; a full round and half a round, or three in flight at three quarters, measured
+// slower on the layer); launches with rows of more than 256 chunks keep half a round
+// with three in flight (70B down: 5% faster than the other); the 1-bit form keeps half
+// a round with four in flight (5% faster than a full round). A partition dispatched
+// later gets its first rows later, so in the 2-bit form each partition's cost is raised
+// by the fraction of the total dispatched before it (1.5-3% on the 8B layer; the 1-bit
+// form measured 5% slower with it).
 template <int FMT>
 hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t stream) {
   constexpr int kCodes = FMT == 0 ? 64 : 128;  // codes per 16-byte chunk
@@ -551,14 +554,14 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     if (attr1 != hipSuccess) return attr1;
     if (attr2 != hipSuccess) return attr2;
   }
-  plan::GemvPlan pl = plan::gemv_plan(N, K, count, kCodes, resident, FMT == 0,
-                                      FMT == 0 && !big ? 3 : 1, FMT == 0 && !big ? 4 : 2);
+  // fraction of a round of resident workgroups (numerator, denominator)
+  const int rnum = FMT == 0 && !big ? 5 : 1, rden = FMT == 0 && !big ? 8 : 2;
+  plan::GemvPlan pl = plan::gemv_plan(N, K, count, kCodes, resident, FMT == 0, rnum, rden);
   {  // fewer workgroups when the activation records' LDS keeps fewer resident
     const size_t need = ((sizeof(unsigned long long) * pl.slots + 15) & ~(size_t)15) + plane_bytes;
     const int cap = bl_device_cus() * max(1, (int)((size_t)160 * 1024 / need));
     if (cap < resident)
-      pl = plan::gemv_plan(N, K, count, kCodes, cap, FMT == 0, FMT == 0 && !big ? 3 : 1,
-                           FMT == 0 && !big ? 4 : 2);
+      pl = plan::gemv_plan(N, K, count, kCodes, cap, FMT == 0, rnum, rden);
   }
   GemvArgs a{};
   for (int o = 0; o < count; ++o) {

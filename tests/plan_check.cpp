@@ -36,12 +36,12 @@ static long g_cases = 0, g_fail = 0;
 static void check_gemv(const int64_t* N, const int64_t* K, int count, int codes, int resident,
                        bool late) {
   ++g_cases;
-  // the 2-bit launch takes 3/4 of the resident workgroups (1/2 with rows of more than
+  // the 2-bit launch takes 5/8 of the resident workgroups (1/2 with rows of more than
   // 256 chunks), the 1-bit one half
   bool big = false;
   for (int i = 0; i < count; ++i) big = big || gemv_cfg((int)(K[i] / codes)).cfg == 5;
   const bool q = codes == 64 && !big;
-  const GemvPlan p = gemv_plan(N, K, count, codes, resident, late, q ? 3 : 1, q ? 4 : 2);
+  const GemvPlan p = gemv_plan(N, K, count, codes, resident, late, q ? 5 : 1, q ? 8 : 2);
   CHECK(p.count == count, "count");
   int next = 0;
   bool seen[kMaxGroup] = {};

@@ -69,11 +69,13 @@ __device__ __forceinline__ void fill_quot(float* quot, float s) {
 // Block-wide double-double sum. Each wave reduces its lanes with DPP into lane 63; after
 // one barrier every wave reduces the per-wave partials itself (DPP over the first NW
 // lanes, zeros beyond), in the same order, so all waves hold the same bits without a
-// second barrier.
+// second barrier. The second level takes only the steps that NW lanes need (2 for 4
+// waves, 3 for 8): the steps it leaves out would add zero pairs, which changes nothing.
 template <int NT>
 __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_hi,
                                              double* sh_lo) {
   constexpr int NW = NT / kWave;
+  constexpr int NL = NW < 4 ? 4 : NW;  // lanes of the second level
   static_assert(NW <= 16, "partials are combined within one DPP row");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   group_dd_sum_to_last<kWave>(hi, lo);
@@ -81,8 +83,8 @@ __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_
   __syncthreads();
   hi = lane < NW ? sh_hi[lane] : 0.0;
   lo = lane < NW ? sh_lo[lane] : 0.0;
-  group_dd_sum_to_last<16>(hi, lo);
-  const double h = readlane_f64(hi, 15), l = readlane_f64(lo, 15);
+  group_dd_sum_to_last<NL>(hi, lo);
+  const double h = readlane_f64(hi, NL - 1), l = readlane_f64(lo, NL - 1);
   hi = h;
   lo = l;
 }
@@ -91,23 +93,34 @@ __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* sh) {
   constexpr int NW = NT / kWave;
+  constexpr int NL = NW < 4 ? 4 : NW;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   v = group_max_to_last<kWave>(v);
   if (lane == kWave - 1) sh[wave] = v;
   __syncthreads();
   float m = lane < NW ? sh[lane] : 0.0f;
-  m = group_max_to_last<16>(m);
-  return readlane_f32(m, 15);
+  m = group_max_to_last<NL>(m);
+  return readlane_f32(m, NL - 1);
 }
 
 // Squares of fp32 values are exact in fp64. Four independent cascaded sums (one per
 // float4 component) keep four dependency chains in flight; they meet at the end.
+// Every term and every running sum is non-negative, so the larger of the two addends
+// is also the larger in magnitude and Dekker's fast two-sum on (max, min) gives the
+// exact rounding error: the same sum and error as Knuth's two-sum, in 5 operations
+// instead of 6.
 struct SumSq4 {
   double h[4] = {0.0, 0.0, 0.0, 0.0}, l[4] = {0.0, 0.0, 0.0, 0.0};
   __device__ __forceinline__ void add(float4 f) {
     const double d[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dd_add1(h[c], l[c], d[c] * d[c]);
+    for (int c = 0; c < 4; ++c) {
+      const double b = d[c] * d[c];
+      const double big = fmax(h[c], b), small = fmin(h[c], b);
+      const double s = big + small;
+      l[c] += small - (s - big);
+      h[c] = s;
+    }
   }
   // one renormalized double-double pair
   __device__ __forceinline__ void total(double& hi, double& lo) {
@@ -284,11 +297,16 @@ hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStre
     // Few rows: latency-bound, each row on one CU, whose four SIMDs do all of its fp64
     // arithmetic. The fewest waves that hold the row: every wave repeats the block
     // reductions, so 512 lanes beat 1024 (4-input decode call 4.6 us against 5.3 us,
-    // same bits), and 256 lanes suit rows of up to 4096 (2.8 us against 3.1).
+    // same bits), and 256 lanes suit rows of up to 4096 (2.8 us against 3.1). Rows of
+    // 14336 (the MLP down projection's input) take an instance that fits them exactly
+    // (7 float4 per lane; with 8 the last eighth of the unrolled work is on zeros):
+    // the 4-input decode call 4.91 -> 4.66 us together with the shorter second
+    // reduction level and the fast two-sum.
     if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ>), grid, dim3(256), 0, stream, a);
     else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ>), grid, dim3(256), 0, stream, a);
     else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ>), grid, dim3(256), 0, stream, a);
     else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<512, 4, FQ>), grid, dim3(512), 0, stream, a);
+    else if (f4 <= 3584) hipLaunchKernelGGL((act_quant_reg<512, 7, FQ>), grid, dim3(512), 0, stream, a);
     else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ>), grid, dim3(512), 0, stream, a);
     else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ>), grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);

@@ -66,8 +66,8 @@ template <int L>
 __device__ __forceinline__ float group_max_to_last(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));
-  v = fmaxf(v, dpp_f32<0x114>(v));
-  v = fmaxf(v, dpp_f32<0x118>(v));
+  if constexpr (L >= 8) v = fmaxf(v, dpp_f32<0x114>(v));
+  if constexpr (L >= 16) v = fmaxf(v, dpp_f32<0x118>(v));
   if constexpr (L >= 32) v = fmaxf(v, dpp_f32<0x142, 0xA>(v));
   if constexpr (L >= 64) v = fmaxf(v, dpp_f32<0x143, 0xC>(v));
   return v;
@@ -126,20 +126,11 @@ __device__ __forceinline__ void group_dd_sum_to_last(double& hi, double& lo) {
   }
   BL_DD_STEP(0xB1)
   BL_DD_STEP(0x4E)
-  BL_DD_STEP(0x114)
-  BL_DD_STEP(0x118)
+  if constexpr (L >= 8) BL_DD_STEP(0x114)
+  if constexpr (L >= 16) BL_DD_STEP(0x118)
   if constexpr (L >= 32) BL_DD_STEP(0x142, 0xA)
   if constexpr (L >= 64) BL_DD_STEP(0x143, 0xC)
 #undef BL_DD_STEP
-}
-
-// Cascaded summation step: hi carries the rounded running sum, lo the sum of the
-// rounding errors (Ogita-Rump-Oishi Sum2).
-__device__ __forceinline__ void dd_add1(double& hi, double& lo, double b) {
-  double s, e;
-  two_sum(hi, b, s, e);
-  hi = s;
-  lo += e;
 }
 
 // ---------------------------------------------------------------- 2-bit codes

@@ -186,7 +186,7 @@ inline void sk_segments(int K, int TB, SkEntry& s) {
 }
 
 // cap: resident workgroups of the skinny kernel (one per CU with its LDS and registers);
-// T: tokens of the launch. A workgroup of projection i with R row blocks per team reads
+// T[i]: tokens of entry i (entries of one launch may differ: token slices of one product). A workgroup of projection i with R row blocks per team reads
 // R * teams * 16 rows of K/4 packed bytes from HBM and the T * K activation bytes of its
 // segments (mostly L2 hits, weighted 1/4 per byte: timelines of the Llama-3-8B layer at
 // T = 16 put the K = 14336 workgroups, with as many activation as weight bytes, ~1.7 us
@@ -212,7 +212,8 @@ inline int64_t sk_wgs_at(const SkEntry& s, const SkCost& c, int64_t tau) {
   return n < c.need ? c.need : n;
 }
 
-inline SkPlan skinny_plan(const int64_t* N, const int64_t* K, int count, int TB, int cap, int T) {
+inline SkPlan skinny_plan(const int64_t* N, const int64_t* K, int count, int TB, int cap,
+                          const int* T) {
   SkPlan p{};
   SkCost c[kMaxGroup];
   int64_t lo = 0, hi = 0;
@@ -223,7 +224,7 @@ inline SkPlan skinny_plan(const int64_t* N, const int64_t* K, int count, int TB,
     s.nrb = (s.N + 15) / 16;
     sk_segments(s.K, TB, s);
     c[i].rowbytes = (int64_t)s.teams * 16 * (K[i] / 4);
-    c[i].act = (int64_t)T * K[i] / kSkActDiv;
+    c[i].act = (int64_t)T[i] * K[i] / kSkActDiv;
     c[i].most = (s.nrb + s.teams - 1) / s.teams;
     const int rcap = kSkTileKB / (s.teams * TB);
     c[i].need = (s.nrb + (int64_t)s.teams * rcap - 1) / ((int64_t)s.teams * rcap);

@@ -75,6 +75,7 @@ struct SkProj {
   int npass;     // passes of a team over the segments
   int R;         // row blocks per team
   int rpg;       // rows per weight scale group
+  int T;         // tokens of this entry (entries may be token slices of one product)
   int wg0, nwg;
 };
 
@@ -82,7 +83,6 @@ struct SkArgs {
   int wg0[BL_GROUP_CAP];  // first workgroup of each projection (INT_MAX when unused)
   SkProj p[BL_GROUP_CAP];
   int count;
-  int T;
   int wbase;  // byte offset of the per-wave weight regroup areas in dynamic LDS
 };
 
@@ -106,6 +106,7 @@ __device__ __forceinline__ SkProj load_sk(SkArgsPtr a, int i) {
   P.npass = a->p[i].npass;
   P.R = a->p[i].R;
   P.rpg = a->p[i].rpg;
+  P.T = a->p[i].T;
   P.wg0 = a->p[i].wg0;
   P.nwg = a->p[i].nwg;
   return P;
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
 #pragma unroll
   for (int i = 1; i < BL_GROUP_CAP; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
   const SkProj P = load_sk(a, pi);
-  const int T = a->T;
+  const int T = P.T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wgl = wg - P.wg0;
   const int nslot = P.teams * P.R;
@@ -433,7 +434,7 @@ int sk_resident(size_t lds) {
 // The dynamic-LDS limit is raised once per instance (first launch), never inside a
 // stream capture after that.
 template <int TB>
-hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
+hipError_t launch_skinny_t(const bl_proj_internal* p, int count, const int* T, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)skinny_kernel<TB>, hipFuncAttributeMaxDynamicSharedMemorySize, kSkLdsCU);
   if (attr != hipSuccess) return attr;
@@ -460,6 +461,7 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
     s.K = e.K;
     s.nrb = e.nrb;
     s.rpg = p[i].rpg;
+    s.T = T[i];
     s.mpw = e.mpw;
     s.nseg = e.nseg;
     s.S = e.S;
@@ -472,7 +474,6 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, int T, hipStrea
   }
   for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
-  a.T = T;
   a.wbase = pl.wbase;
   const int wgs = pl.wgs;
   const size_t lds = pl.lds;
@@ -489,23 +490,60 @@ bool bl_skinny_supports(int T, int64_t N, int K) {
   return T >= 1 && T <= 128 && K % 256 == 0 && N * 64 * 4 < (int64_t(1) << 31);
 }
 
-// Up to 64 tokens in one launch (one, two or four token blocks of 16); more run as passes
-// over slices of 64 tokens (each pass streams the weights again: the choice of the
-// caller when the GEMM's tiles would leave most of the device idle).
+// Token blocks per slice for a pass of tn tokens over a projection of N x K: the slices
+// of one pass are entries of one grouped launch that read the same weights, so a slice
+// beyond the first mostly re-reads them from the caches while each slice keeps its
+// activations in one pass over K (wide slices reload theirs per pass when 256 * MPW
+// codes per wave do not cover K). Measured on one box (us per product, graph replays,
+// rotating weight copies, bit-identical outputs), one slice / halves of 32 / slices of 16:
+//   N x K, packed bytes       24 tokens          32 tokens          48 tokens          64 tokens
+//   28672 x 8192, 58.7 MB     20.9 / - / 22.9    22.4 / - / 22.6    30.8 / 30.6 / 38.4 33.7 / 29.8 / 35.1
+//   28672 x 4096, 29.4 MB     15.5 / - / 14.6    16.9 / - / 14.7    20.4 / 20.9 / 21.3 21.1 / 21.2 / 21.6
+//   4096 x 14336, 14.7 MB     15.9 / - / 13.5    18.6 / - / 13.6    27.3 / 21.9 / 16.5 32.6 / 21.1 / 16.9
+//   6144 x 4096, 12.6 MB      10.2 / - / 8.4     11.5 / - / 8.6     11.4 / 12.9 / 10.0 12.8 / 13.1 / 10.3
+// So: slices of 16 for long rows (K >= 14336) and small matrices (up to 16 MB, or up to
+// 32 MB for at most 32 tokens); halves of 32 for larger matrices beyond 32 tokens;
+// otherwise one slice.
+static int sk_slice_tb(int tn, int64_t N, int64_t K) {
+  const int64_t bytes = N * (K / 4);
+  const int one = tn <= 16 ? 1 : tn <= 32 ? 2 : 4;
+  if (tn <= 16) return 1;
+  if (K >= 14336 || bytes <= ((int64_t)16 << 20)) return 1;
+  if (tn <= 32) return bytes <= ((int64_t)32 << 20) ? 1 : 2;
+  return bytes > ((int64_t)32 << 20) ? 2 : one;
+}
+
+// Up to 64 tokens in one launch, more as passes of 64 (each pass streams the weights
+// again: the caller's choice when the GEMM's tiles would leave most of the device idle).
+// A pass of tn tokens runs as slices of 16 * TB tokens, each slice an entry of one
+// grouped launch of the TB kernel (the last slice ragged); the largest projection of a
+// grouped call picks TB, and with more entries than a launch takes, one slice per pass.
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
   for (int t0 = 0; t0 < T; t0 += 64) {
     const int tn = T - t0 < 64 ? T - t0 : 64;
+    int big = 0;
+    for (int i = 1; i < count; ++i)
+      if ((int64_t)p[i].N * p[i].K > (int64_t)p[big].N * p[big].K) big = i;
+    int TB = sk_slice_tb(tn, p[big].N, p[big].K);
+    const int per = 16 * TB, slices = (tn + per - 1) / per;
+    if (slices * count > BL_GROUP_CAP) TB = tn <= 16 ? 1 : tn <= 32 ? 2 : 4;
+    const int ns = (tn + 16 * TB - 1) / (16 * TB);
     bl_proj_internal q[BL_GROUP_CAP];
-    for (int i = 0; i < count; ++i) {
-      q[i] = p[i];
-      q[i].Xq += (int64_t)t0 * p[i].K;
-      q[i].x_scale += t0;
-      q[i].Y += (int64_t)t0 * p[i].N;
-      if (q[i].acc) q[i].acc += (int64_t)t0 * p[i].N;
-    }
-    const hipError_t e = tn <= 16   ? launch_skinny_t<1>(q, count, tn, stream)
-                         : tn <= 32 ? launch_skinny_t<2>(q, count, tn, stream)
-                                    : launch_skinny_t<4>(q, count, tn, stream);
+    int Ts[BL_GROUP_CAP];
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+      for (int j = 0; j < ns; ++j) {
+        const int a = t0 + j * 16 * TB, tj = min(16 * TB, t0 + tn - a);
+        q[n] = p[i];
+        q[n].Xq += (int64_t)a * p[i].K;
+        q[n].x_scale += a;
+        q[n].Y += (int64_t)a * p[i].N;
+        if (q[n].acc) q[n].acc += (int64_t)a * p[i].N;
+        Ts[n++] = tj;
+      }
+    const hipError_t e = TB == 1   ? launch_skinny_t<1>(q, n, Ts, stream)
+                         : TB == 2 ? launch_skinny_t<2>(q, n, Ts, stream)
+                                   : launch_skinny_t<4>(q, n, Ts, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -105,9 +105,10 @@ static void check_gemv(const int64_t* N, const int64_t* K, int count, int codes,
 // The kernel (bl_skinny.hip): team tg = wgl * teams + team of TT = nwg * teams takes row
 // blocks rb = tg + fr * TT (fr < R); wave seg of a team takes segment p * S + seg in pass
 // p < npass; a segment is 256 * mpw codes of K.
-static void check_skinny(const int64_t* N, const int64_t* K, int count, int TB, int cap, int T) {
+static void check_skinny(const int64_t* N, const int64_t* K, int count, int TB, int cap,
+                         const int* Ts) {
   ++g_cases;
-  const SkPlan p = skinny_plan(N, K, count, TB, cap, T);
+  const SkPlan p = skinny_plan(N, K, count, TB, cap, Ts);
   int next = 0;
   for (int i = 0; i < count; ++i) {
     const SkEntry& e = p.e[i];
@@ -137,6 +138,8 @@ static void check_skinny(const int64_t* N, const int64_t* K, int count, int TB, 
           (long long)N[i], (long long)K[i], bad);
     CHECK((int64_t)(e.nwg - 1) * e.teams < e.nrb, "a workgroup without a row block");
     // 32-bit buffer ranges: activations T*K, outputs T*N*4, a row block 16 rows of K/4
+    const int T = Ts[i];
+    CHECK(T >= 1 && T <= 16 * TB, "entry %d: %d tokens in %d token blocks", i, T, TB);
     CHECK((int64_t)T * K[i] < (int64_t(1) << 32), "activation range");
     CHECK((int64_t)T * N[i] * 4 < (int64_t(1) << 31), "output range");
     CHECK((int64_t)16 * (K[i] / 4) < (int64_t(1) << 31), "weight range");
@@ -246,7 +249,7 @@ int main() {
     for (int TB = 1; TB <= 4; TB *= 2)
       for (int64_t n : rows)
         for (int64_t k : sks)
-          for (int T : {8 * TB + 1, 16 * TB}) check_skinny(&n, &k, 1, TB, cap, T);
+          for (int T : {8 * TB + 1, 16 * TB}) check_skinny(&n, &k, 1, TB, cap, &T);
   {
     const int64_t N7[] = {4096, 1024, 1024, 4096, 14336, 14336, 4096};
     const int64_t K7[] = {4096, 4096, 4096, 4096, 4096, 4096, 14336};
@@ -257,10 +260,30 @@ int main() {
     for (int cap : caps)
       for (int TB = 1; TB <= 4; TB *= 2)
         for (int T : {8 * TB + 1, 16 * TB}) {
-          check_skinny(N7, K7, 7, TB, cap, T);
-          check_skinny(N4, K4, 4, TB, cap, T);
-          check_skinny(Nm, Km, 8, TB, cap, T);
+          const int Ts[8] = {T, T, T, T, T, T, T, T};
+          check_skinny(N7, K7, 7, TB, cap, Ts);
+          check_skinny(N4, K4, 4, TB, cap, Ts);
+          check_skinny(Nm, Km, 8, TB, cap, Ts);
         }
+    // token slices of one product as entries of one launch: the first slices full, the
+    // last one ragged (as the launcher cuts 17..64 tokens)
+    for (int cap : caps)
+      for (int TB = 1; TB <= 2; TB *= 2)
+        for (int last : {1, 8 * TB + 3, 16 * TB})
+          for (int parts = 2; parts <= 4; ++parts) {
+            int64_t Ns[8], Ks[8];
+            int Ts[8];
+            for (int j = 0; j < parts; ++j) {
+              Ns[j] = N4[2];
+              Ks[j] = K4[2];
+              Ts[j] = j + 1 < parts ? 16 * TB : last;
+              Ns[parts + j] = N4[3];
+              Ks[parts + j] = 28672;
+              Ts[parts + j] = Ts[j];
+            }
+            check_skinny(Ns, Ks, parts, TB, cap, Ts);
+            check_skinny(Ns, Ks, 2 * parts, TB, cap, Ts);
+          }
   }
   // split K and the XCD-major tile numbering
   const int cuss[] = {256, 304, 80};

@@ -396,6 +396,33 @@ def test_prefill_full_size_sampled(bl, N, K):
     assert np.array_equal(acch[toks], acc_t)
 
 
+# 17..64 tokens run as token slices of 16 or 32 (entries of one grouped launch over the
+# same weights, the last slice ragged) or as one slice, by shape: each way at full size,
+# all tokens on sampled rows and all rows on sampled tokens
+@pytest.mark.parametrize("T,N,K", [(50, 28672, 8192), (48, 28672, 4096), (24, 28672, 8192),
+                                   (61, 4096, 14336), (40, 6144, 4096), (17, 4096, 14336)])
+def test_skinny_token_slices_sampled(bl, T, N, K):
+    print("skinny slices T=%d N=%d K=%d" % (T, N, K), flush=True)
+    r = np.random.default_rng(T + N + K)
+    Xq = r.integers(-127, 128, size=(T, K)).astype(np.int8)
+    q = r.integers(-1, 2, size=(N, K)).astype(np.int8)
+    P = oracle.pack(q)
+    del q
+    xs = r.uniform(1.0, 300.0, T).astype(np.float32)
+    beta = np.float32(0.02)
+    Y = torch.empty((T, N), dtype=torch.float32, device=DEV)
+    acc = torch.empty((T, N), dtype=torch.int32, device=DEV)
+    bl.bitlinear_forward_ex(dev(Xq), dev(xs), dev(P), dev(np.array([beta])), Y, acc, kernel="skinny")
+    Yh, acch = host(Y), host(acc)
+    rows = np.unique(np.concatenate([r.choice(N, 64, replace=False), [0, N - 1]]))
+    acc_o = oracle.product(Xq, P[rows], K)
+    assert np.array_equal(acch[:, rows], acc_o)
+    assert_y_close(Yh[:, rows], oracle.rescale(acc_o, xs, beta), "slices")
+    toks = np.unique(np.array([0, 15, 16, 31, 32, 47, 48, T - 1]).clip(0, T - 1))
+    acc_t = oracle.product(Xq[toks], P, K)
+    assert np.array_equal(acch[toks], acc_t)
+
+
 @pytest.mark.parametrize("which", ["down", "gate"])
 def test_sweep70b_full_size_sampled(bl, which):
     N, K = workloads.LLAMA_70B_SWEEP[which]

@@ -131,6 +131,7 @@ inline GemvPlan gemv_plan(const int64_t* N, const int64_t* K, int count, int cod
 
 // ---------------------------------------------------------------- skinny MFMA product
 constexpr int kSkWaves = 8;                     // waves per workgroup (512 threads)
+constexpr int kSkEntries = 2 * kMaxGroup;       // entries of one launch: projections x token slices
 constexpr int kSkTileKB = 96;                   // LDS for the partial tiles, KiB
 constexpr size_t kSkLdsMax = kSkTileKB * 1024 + 96 * 4 + 32 * 4;
 constexpr int kSkLdsCU = 160 * 1024;            // LDS of one CU
@@ -149,7 +150,7 @@ struct SkEntry {
 };
 
 struct SkPlan {
-  SkEntry e[kMaxGroup];
+  SkEntry e[kSkEntries];
   int count;
   int wgs;
   size_t tile_lds;  // LDS for tiles, counts and factors
@@ -215,7 +216,7 @@ inline int64_t sk_wgs_at(const SkEntry& s, const SkCost& c, int64_t tau) {
 inline SkPlan skinny_plan(const int64_t* N, const int64_t* K, int count, int TB, int cap,
                           const int* T) {
   SkPlan p{};
-  SkCost c[kMaxGroup];
+  SkCost c[kSkEntries];
   int64_t lo = 0, hi = 0;
   for (int i = 0; i < count; ++i) {
     SkEntry& s = p.e[i];

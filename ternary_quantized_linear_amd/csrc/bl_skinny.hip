@@ -80,8 +80,8 @@ struct SkProj {
 };
 
 struct SkArgs {
-  int wg0[BL_GROUP_CAP];  // first workgroup of each projection (INT_MAX when unused)
-  SkProj p[BL_GROUP_CAP];
+  int wg0[plan::kSkEntries];  // first workgroup of each entry (INT_MAX when unused)
+  SkProj p[plan::kSkEntries];
   int count;
   int wbase;  // byte offset of the per-wave weight regroup areas in dynamic LDS
 };
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   const int wg = (int)blockIdx.x;
   int pi = 0;
 #pragma unroll
-  for (int i = 1; i < BL_GROUP_CAP; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
+  for (int i = 1; i < plan::kSkEntries; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
   const SkProj P = load_sk(a, pi);
   const int T = P.T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -440,7 +440,7 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, const int* T, h
   if (attr != hipSuccess) return attr;
   // one workgroup per CU: its registers and, with the regroup areas, its LDS bound it
   const int cap = sk_resident<TB>(kSkLdsMax + 16 + kSkRegroup);
-  int64_t N[BL_GROUP_CAP], K[BL_GROUP_CAP];
+  int64_t N[plan::kSkEntries], K[plan::kSkEntries];
   for (int i = 0; i < count; ++i) {
     N[i] = p[i].N;
     K[i] = p[i].K;
@@ -472,7 +472,7 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, const int* T, h
     s.wg0 = e.wg0;
     a.wg0[i] = e.wg0;
   }
-  for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
+  for (int i = count; i < plan::kSkEntries; ++i) a.wg0[i] = INT_MAX;
   a.count = count;
   a.wbase = pl.wbase;
   const int wgs = pl.wgs;
@@ -517,19 +517,25 @@ static int sk_slice_tb(int tn, int64_t N, int64_t K) {
 // again: the caller's choice when the GEMM's tiles would leave most of the device idle).
 // A pass of tn tokens runs as slices of 16 * TB tokens, each slice an entry of one
 // grouped launch of the TB kernel (the last slice ragged); the largest projection of a
-// grouped call picks TB, and with more entries than a launch takes, one slice per pass.
+// grouped call picks TB.
 hipError_t bl_launch_skinny(const bl_proj_internal* p, int count, int T, hipStream_t stream) {
   for (int t0 = 0; t0 < T; t0 += 64) {
     const int tn = T - t0 < 64 ? T - t0 : 64;
     int big = 0;
     for (int i = 1; i < count; ++i)
       if ((int64_t)p[i].N * p[i].K > (int64_t)p[big].N * p[big].K) big = i;
+    const int whole = tn <= 16 ? 1 : tn <= 32 ? 2 : 4;  // one slice
     int TB = sk_slice_tb(tn, p[big].N, p[big].K);
-    const int per = 16 * TB, slices = (tn + per - 1) / per;
-    if (slices * count > BL_GROUP_CAP) TB = tn <= 16 ? 1 : tn <= 32 ? 2 : 4;
+    const int per = 16 * TB, slices = (tn + per - 1) / per, last = tn - (slices - 1) * per;
+    // a short last slice costs nearly a full pass over the weights (the 8B layer's seven
+    // projections at 17 / 20 / 24 tokens: 26.0 / 25.4 / 24.3 us in slices of 16 against
+    // 21.2 / 22.1 / 23.3 in one, 24.8 against 26.5 at 32): slices need a last one of at
+    // least 8 tokens, and in a grouped call (whose many partitions do not keep the
+    // slices' workgroups on the same XCDs) every slice full
+    if (slices * count > plan::kSkEntries || last < 8 || (count > 1 && last < per)) TB = whole;
     const int ns = (tn + 16 * TB - 1) / (16 * TB);
-    bl_proj_internal q[BL_GROUP_CAP];
-    int Ts[BL_GROUP_CAP];
+    bl_proj_internal q[plan::kSkEntries];
+    int Ts[plan::kSkEntries];
     int n = 0;
     for (int i = 0; i < count; ++i)
       for (int j = 0; j < ns; ++j) {

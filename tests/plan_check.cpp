@@ -284,6 +284,21 @@ int main() {
             check_skinny(Ns, Ks, parts, TB, cap, Ts);
             check_skinny(Ns, Ks, 2 * parts, TB, cap, Ts);
           }
+    // the seven projections of a layer in two slices each: sixteen entries at most
+    for (int cap : caps)
+      for (int last : {1, 9, 16}) {
+        int64_t Ns[16], Ks[16];
+        int Ts[16];
+        for (int j = 0; j < 14; ++j) {
+          Ns[j] = N7[j / 2];
+          Ks[j] = K7[j / 2];
+          Ts[j] = j % 2 ? last : 16;
+        }
+        Ns[14] = Nm[3]; Ks[14] = Km[3]; Ts[14] = 16;
+        Ns[15] = Nm[6]; Ks[15] = Km[6]; Ts[15] = last;
+        check_skinny(Ns, Ks, 14, 1, cap, Ts);
+        check_skinny(Ns, Ks, 16, 1, cap, Ts);
+      }
   }
   // split K and the XCD-major tile numbering
   const int cuss[] = {256, 304, 80};

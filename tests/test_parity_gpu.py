@@ -400,7 +400,8 @@ def test_prefill_full_size_sampled(bl, N, K):
 # same weights, the last slice ragged) or as one slice, by shape: each way at full size,
 # all tokens on sampled rows and all rows on sampled tokens
 @pytest.mark.parametrize("T,N,K", [(50, 28672, 8192), (48, 28672, 4096), (24, 28672, 8192),
-                                   (61, 4096, 14336), (40, 6144, 4096), (17, 4096, 14336)])
+                                   (61, 4096, 14336), (40, 6144, 4096), (26, 4096, 14336),
+                                   (17, 4096, 14336)])
 def test_skinny_token_slices_sampled(bl, T, N, K):
     print("skinny slices T=%d N=%d K=%d" % (T, N, K), flush=True)
     r = np.random.default_rng(T + N + K)

@@ -98,7 +98,7 @@ def test_scale_groups_end_to_end_and_grouped_call(bl):
         assert_y_close(host(Yi), ri["Y"], "grouped call")
 
 
-@pytest.mark.parametrize("T", [1, 16, 24, 48])
+@pytest.mark.parametrize("T", [1, 16, 24, 32, 48])
 def test_fused_layer_layout_prepared(bl, T):
     # The decode layer in one allocation (reading L1): q|k|v and gate|up each quantized
     # per projection into consecutive rows, one scale per segment (rows per group = gcd

@@ -162,8 +162,9 @@ __device__ __forceinline__ uint32_t quant4(float4 y, float s) {
   return lo | hi;
 }
 
-// Row held in registers: lane i owns float4 i, i+NT, ..., i+(VPT-1)NT of the row.
-template <int NT, int VPT, bool FQ>
+// Row held in registers: lane i owns float4 i, i+NT, ..., i+(VPT-1)NT of the row. GAIN:
+// the instance for calls with a gain (it holds the gain's float4 as well).
+template <int NT, int VPT, bool FQ, bool GAIN>
 __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   __shared__ double sh_hi[NT / kWave], sh_lo[NT / kWave];
   __shared__ float sh_m[NT / kWave];
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   const int t = blockIdx.x;
   const int K4 = e.K >> 2;
   const float4* x4 = reinterpret_cast<const float4*>(e.X + (int64_t)t * e.K);
-  const bool has_gain = e.gain != nullptr && !a.no_norm;
+  const bool has_gain = GAIN && e.gain != nullptr && !a.no_norm;
   const float4* g4 = reinterpret_cast<const float4*>(e.gain);
   // the row is loaded once, up front; the gain (shared by every row, so cache-resident)
   // only where the norm needs it, which keeps it out of the registers that hold the row
@@ -185,6 +186,15 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
     SumSq4 acc;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) acc.add(v[j]);
+    // With a gain and room in the registers, the gain's float4 are all asked for here, so
+    // that they arrive during the block reduction (loaded where the norm uses them, each
+    // load is waited for before the next is issued: seven round trips for a row of 14336)
+    constexpr bool kPre = GAIN && VPT <= 8;
+    float4 gv[kPre ? VPT : 1];
+    if (kPre && has_gain) {
+#pragma unroll
+      for (int j = 0; j < (kPre ? VPT : 0); ++j) gv[j] = g4[min((int)threadIdx.x + j * NT, K4 - 1)];
+    }
     double hi, lo;
     acc.total(hi, lo);
     block_dd_sum<NT>(hi, lo, sh_hi, sh_lo);
@@ -194,7 +204,8 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         int i = threadIdx.x + j * NT;
-        v[j] = norm4(v[j], r, i < K4 ? g4[i] : make_float4(1.f, 1.f, 1.f, 1.f), true);
+        if constexpr (kPre) v[j] = norm4(v[j], r, gv[j], true);  // lanes past K4 store nothing
+        else v[j] = norm4(v[j], r, i < K4 ? g4[i] : make_float4(1.f, 1.f, 1.f, 1.f), true);
       }
     } else {
 #pragma unroll
@@ -289,8 +300,8 @@ using namespace bl;
 
 namespace {
 
-template <bool FQ>
-hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStream_t stream) {
+template <bool FQ, bool G>
+hipError_t launch_acts_g(const ActArgs& a, int maxK, int64_t T, int count, hipStream_t stream) {
   dim3 grid((unsigned)T, (unsigned)count);
   const int f4 = (maxK + 3) / 4;  // float4 per row
   if (T <= 64) {
@@ -302,25 +313,34 @@ hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStre
     // (7 float4 per lane; with 8 the last eighth of the unrolled work is on zeros):
     // the 4-input decode call 4.91 -> 4.66 us together with the shorter second
     // reduction level and the fast two-sum.
-    if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ>), grid, dim3(256), 0, stream, a);
-    else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ>), grid, dim3(256), 0, stream, a);
-    else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ>), grid, dim3(256), 0, stream, a);
-    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<512, 4, FQ>), grid, dim3(512), 0, stream, a);
-    else if (f4 <= 3584) hipLaunchKernelGGL((act_quant_reg<512, 7, FQ>), grid, dim3(512), 0, stream, a);
-    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ>), grid, dim3(512), 0, stream, a);
-    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ>), grid, dim3(512), 0, stream, a);
+    if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ, G>), grid, dim3(256), 0, stream, a);
+    else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ, G>), grid, dim3(256), 0, stream, a);
+    else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ, G>), grid, dim3(256), 0, stream, a);
+    else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<512, 4, FQ, G>), grid, dim3(512), 0, stream, a);
+    else if (f4 <= 3584) hipLaunchKernelGGL((act_quant_reg<512, 7, FQ, G>), grid, dim3(512), 0, stream, a);
+    else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ, G>), grid, dim3(512), 0, stream, a);
+    else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ, G>), grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
   }
   // many rows: throughput-bound; the smallest register footprint that holds the row
-  if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<256, 8, FQ>), grid, dim3(256), 0, stream, a);
-  else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ>), grid, dim3(512), 0, stream, a);
-  else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ>), grid, dim3(512), 0, stream, a);
+  if (f4 <= 256) hipLaunchKernelGGL((act_quant_reg<256, 1, FQ, G>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 512) hipLaunchKernelGGL((act_quant_reg<256, 2, FQ, G>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 1024) hipLaunchKernelGGL((act_quant_reg<256, 4, FQ, G>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 2048) hipLaunchKernelGGL((act_quant_reg<256, 8, FQ, G>), grid, dim3(256), 0, stream, a);
+  else if (f4 <= 4096) hipLaunchKernelGGL((act_quant_reg<512, 8, FQ, G>), grid, dim3(512), 0, stream, a);
+  else if (f4 <= 8192) hipLaunchKernelGGL((act_quant_reg<512, 16, FQ, G>), grid, dim3(512), 0, stream, a);
   else hipLaunchKernelGGL((act_quant_stream<1024, FQ>), grid, dim3(1024), 0, stream, a);
   return hipGetLastError();
+}
+
+// the gain instances when an entry has a gain and the norm is on
+template <bool FQ>
+hipError_t launch_acts(const ActArgs& a, int maxK, int64_t T, int count, hipStream_t stream) {
+  bool gain = false;
+  for (int i = 0; i < count; ++i) gain = gain || (a.e[i].gain != nullptr && !a.no_norm);
+  return gain ? launch_acts_g<FQ, true>(a, maxK, T, count, stream)
+              : launch_acts_g<FQ, false>(a, maxK, T, count, stream);
 }
 
 }  // namespace

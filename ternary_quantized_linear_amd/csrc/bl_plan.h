@@ -62,7 +62,10 @@ struct GemvPlan {
 
 // Relative cost of a byte streamed by segmented rows (S waves meet per row in LDS and an
 // eighth of a segment's lanes may idle) against a byte of a one-wave row, in 1/16.
-constexpr int kGemvSegCost16 = 20;
+// Per-wave end times of the 8B layer (K = 14336 rows segmented, the others not) showed
+// the segmented partition's waves ending ~2.4 us (median) before the others at 20/16;
+// 18/16 and 19/16 measured 2-3% faster than 20/16 (alternating runs, two boxes).
+constexpr int kGemvSegCost16 = 18;
 
 // N[i], K[i]: the projections; codes: codes per 16-byte chunk (64 for 2-bit, 128 for
 // 1-bit weights); resident: workgroups of the kernel the device keeps resident at once.

@@ -89,6 +89,34 @@ __device__ __forceinline__ void block_dd_sum(double& hi, double& lo, double* sh_
   lo = l;
 }
 
+// The double-double sum and the maximum of non-negative values together: both wave
+// reductions (independent chains), one LDS round and one barrier, then both second levels.
+template <int NT>
+__device__ __forceinline__ void block_dd_sum_max(double& hi, double& lo, float& mx, double* sh_hi,
+                                                 double* sh_lo, float* sh_m) {
+  constexpr int NW = NT / kWave;
+  constexpr int NL = NW < 4 ? 4 : NW;
+  static_assert(NW <= 16, "partials are combined within one DPP row");
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  group_dd_sum_to_last<kWave>(hi, lo);
+  mx = group_max_to_last<kWave>(mx);
+  if (lane == kWave - 1) {
+    sh_hi[wave] = hi;
+    sh_lo[wave] = lo;
+    sh_m[wave] = mx;
+  }
+  __syncthreads();
+  hi = lane < NW ? sh_hi[lane] : 0.0;
+  lo = lane < NW ? sh_lo[lane] : 0.0;
+  float m = lane < NW ? sh_m[lane] : 0.0f;
+  group_dd_sum_to_last<NL>(hi, lo);
+  m = group_max_to_last<NL>(m);
+  const double h = readlane_f64(hi, NL - 1), l = readlane_f64(lo, NL - 1);
+  hi = h;
+  lo = l;
+  mx = readlane_f32(m, NL - 1);
+}
+
 // Block-wide maximum of non-negative values, same structure.
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* sh) {
@@ -181,6 +209,32 @@ __global__ __launch_bounds__(NT) void act_quant_reg(ActArgs a) {
   for (int j = 0; j < VPT; ++j) {
     int i = threadIdx.x + j * NT;
     v[j] = i < K4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (!a.no_norm && !has_gain && !FQ) {
+    // Without a gain, y = fp32(fp64(x) * r) is two roundings of a product that grows with
+    // |x|, each rounding monotone and odd, so max|y| = fp32(fp64(max|x|) * r) exactly: the
+    // maximum rides with the sum of squares through one block reduction (one barrier
+    // instead of two), and y is formed where it is quantized.
+    SumSq4 acc;
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      acc.add(v[j]);
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    }
+    double hi, lo;
+    acc.total(hi, lo);
+    block_dd_sum_max<NT>(hi, lo, mx, sh_hi, sh_lo, sh_m);
+    const double r = 1.0 / sqrt(hi / (double)e.K + (double)a.eps);
+    const float s = 127.0f / fmaxf((float)((double)mx * r), 1e-5f);
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(e.Xq + (int64_t)t * e.K);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      int i = threadIdx.x + j * NT;
+      if (i < K4) q4[i] = quant4(norm4(v[j], r, make_float4(1.f, 1.f, 1.f, 1.f), false), s);
+    }
+    if (threadIdx.x == 0) e.s[t] = s;
+    return;
   }
   if (!a.no_norm) {
     SumSq4 acc;

@@ -264,7 +264,11 @@ __device__ __forceinline__ void load_act_chunk(const int8_t* x, int c, bool on, 
 // workgroup's.
 template <int FMT, int NR>
 __device__ __forceinline__ void publish_acts(const GemvProj& P, uint8_t* plds, int* psum,
-                                             const uint4 (&araw)[NR]) {
+                                             const uint4 (&araw)[NR], unsigned long long* slots,
+                                             int nslots) {
+  // segmented rows: the combine words start at zero; cleared here, before the one barrier
+  // that also publishes the activations (the weight ring is already in flight)
+  for (int i = threadIdx.x; i < nslots; i += kGemvThreads) slots[i] = 0ull;
   for (int c = threadIdx.x; c < P.C; c += kGemvThreads) {
     uint4 v[NR];
     if (c == (int)threadIdx.x) {
@@ -289,7 +293,7 @@ __device__ __forceinline__ void publish_acts(const GemvProj& P, uint8_t* plds, i
 
 template <int L, int I, int S, int FMT, int MAXI>
 __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
-                                      unsigned long long* slots, int plane_base) {
+                                      unsigned long long* slots, int plane_base, int nslots) {
   constexpr int RW = kWave / L;        // rows per row group
   constexpr int GPW = kGemvWaves / S;  // row groups per workgroup step
   const int lane = threadIdx.x & (kWave - 1);
@@ -313,7 +317,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
     else load_raw0(P.Xq, threadIdx.x, araw);
   }
   if (g0 >= ngroups) {
-    publish_acts<FMT, NR>(P, plds, psum, araw);
+    publish_acts<FMT, NR>(P, plds, psum, araw, slots, nslots);
     return;
   }
   const int glast = g0 + ((ngroups - 1 - g0) / stride) * stride;
@@ -365,7 +369,7 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
   uint4 x[FMT == 0 ? I : 1][4];
   uint32_t x1[FMT == 1 ? I : 1][4][8];
   int xsum = 0;
-  publish_acts<FMT, NR>(P, plds, psum, araw);
+  publish_acts<FMT, NR>(P, plds, psum, araw, slots, nslots);
 #pragma unroll
   for (int i = 0; i < I; ++i) {
     if constexpr (FMT == 0) read_chunk0(plds, ci[i], on[i], x[i]);
@@ -480,19 +484,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
   // branches and the row bases in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wgl = wg - P.wg0;
-  if (P.cfg >= 3) {  // segmented rows: clear the combine words
-    for (int i = threadIdx.x; i < a->slots; i += kGemvThreads) slots[i] = 0ull;
-    __syncthreads();
-  }
+  const int ns = P.cfg >= 3 ? a->slots : 0;  // combine words to clear (segmented rows)
   const int pb = (8 * a->slots + 15) & ~15;  // 1-bit planes after the combine words
   switch (P.cfg) {
-    case 0: sweep<16, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 16
-    case 1: sweep<32, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 32
-    case 2: sweep<64, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 64
-    case 3: sweep<64, 1, 2, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 128
-    case 4: sweep<64, 1, 4, FMT, MAXI>(P, wgl, wave, slots, pb); break;  // C <= 256
+    case 0: sweep<16, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 16
+    case 1: sweep<32, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 32
+    case 2: sweep<64, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 64
+    case 3: sweep<64, 1, 2, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 128
+    case 4: sweep<64, 1, 4, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 256
     default:
-      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT, MAXI>(P, wgl, wave, slots, pb);  // C <= 512
+      if constexpr (MAXI >= 2) sweep<64, 2, 4, FMT, MAXI>(P, wgl, wave, slots, pb, ns);  // C <= 512
       break;
   }
 }

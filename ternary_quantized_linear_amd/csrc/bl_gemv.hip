@@ -48,6 +48,7 @@
 #include "bl_plan.h"
 
 #include <climits>
+#include <cstddef>
 
 namespace bl {
 
@@ -80,13 +81,23 @@ struct GemvProj {
 };
 
 struct GemvArgs {
-  int wg0[BL_GROUP_CAP];  // first workgroup of each projection (one scalar load)
   GemvProj p[BL_GROUP_CAP];
   int count;
-  int slots;  // 64-bit combine words per workgroup (0: no segmented rows)
 };
 
 typedef const GemvArgs __attribute__((address_space(4)))* ArgsPtr;
+
+// The kernel's argument list: the partition starts and the combine-word count come first,
+// as scalars, so that they can be preloaded into SGPRs at wave launch (the build asks
+// for 8 preloaded dwords): a wave then finds its projection without a round trip to the
+// argument memory, and the projection's fields are its first load.
+struct GemvKernArgs {
+  int wg0[BL_GROUP_CAP - 1];  // first workgroup of projections 1..7 (INT_MAX when unused)
+  int slots;                  // 64-bit combine words per workgroup (0: no segmented rows)
+  GemvArgs g;
+};
+constexpr int kGemvArgsOffset = 32;
+static_assert(offsetof(GemvKernArgs, g) == kGemvArgsOffset, "argument layout");
 
 // Field-by-field copy out of the constant (kernel-argument) address space.
 __device__ __forceinline__ GemvProj load_proj(ArgsPtr a, int i) {
@@ -471,21 +482,23 @@ __device__ __forceinline__ void sweep(const GemvProj& P, int wgl, int wave,
 // MAXI = 2 adds the mapping for rows of more than 256 chunks (two chunks per lane);
 // the MAXI = 1 instance leaves it out so that its register budget stays small.
 template <int MAXI, int FMT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs) {
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(int w1, int w2, int w3, int w4,
+                                                            int w5, int w6, int w7, int nslots,
+                                                            GemvArgs) {
   extern __shared__ unsigned long long slots[];
-  const ArgsPtr a = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  const ArgsPtr a = (ArgsPtr)((const char __attribute__((address_space(4)))*)
+                                  __builtin_amdgcn_kernarg_segment_ptr() + kGemvArgsOffset);
   const int wg = (int)blockIdx.x;
-  // wg0 ascends, unused entries hold INT_MAX: the projection is the count of starts <= wg
-  int pi = 0;
-#pragma unroll
-  for (int i = 1; i < BL_GROUP_CAP; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
+  // the starts ascend, unused ones are INT_MAX: the projection is the count of starts <= wg
+  const int pi = (wg >= w1) + (wg >= w2) + (wg >= w3) + (wg >= w4) + (wg >= w5) + (wg >= w6) +
+                 (wg >= w7);
   const GemvProj P = load_proj(a, pi);
   // the wave index is uniform per wave: readfirstlane keeps the row schedule, the
   // branches and the row bases in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wgl = wg - P.wg0;
-  const int ns = P.cfg >= 3 ? a->slots : 0;  // combine words to clear (segmented rows)
-  const int pb = (8 * a->slots + 15) & ~15;  // 1-bit planes after the combine words
+  const int ns = P.cfg >= 3 ? nslots : 0;  // combine words to clear (segmented rows)
+  const int pb = (8 * nslots + 15) & ~15;  // 1-bit planes after the combine words
   switch (P.cfg) {
     case 0: sweep<16, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 16
     case 1: sweep<32, 1, 1, FMT, MAXI>(P, wgl, wave, slots, pb, ns); break;  // C <= 32
@@ -564,7 +577,8 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     if (cap < resident)
       pl = plan::gemv_plan(N, K, count, kCodes, cap, FMT == 0, rnum, rden);
   }
-  GemvArgs a{};
+  GemvKernArgs ka{};
+  GemvArgs& a = ka.g;
   for (int o = 0; o < count; ++o) {
     const plan::GemvEntry& e = pl.e[o];
     const bl_proj_internal& q = p[e.src];
@@ -582,18 +596,19 @@ hipError_t launch_gemv_fmt(const bl_proj_internal* p, int count, hipStream_t str
     g.rpg = q.rpg;
     g.nwg = e.nwg;
     g.wg0 = e.wg0;
-    a.wg0[o] = e.wg0;
+    if (o > 0) ka.wg0[o - 1] = e.wg0;
   }
-  for (int i = count; i < BL_GROUP_CAP; ++i) a.wg0[i] = INT_MAX;
+  for (int i = max(count, 1); i < BL_GROUP_CAP; ++i) ka.wg0[i - 1] = INT_MAX;
   a.count = count;
-  a.slots = pl.slots;
+  ka.slots = pl.slots;
   const size_t lds = ((sizeof(unsigned long long) * (size_t)pl.slots + 15) & ~(size_t)15) + plane_bytes;
+  const int* w = ka.wg0;
   if (pl.big)
     hipLaunchKernelGGL((gemv_kernel<2, FMT>), dim3((unsigned)pl.wgs), dim3(kGemvThreads), lds, stream,
-                       a);
+                       w[0], w[1], w[2], w[3], w[4], w[5], w[6], ka.slots, a);
   else
     hipLaunchKernelGGL((gemv_kernel<1, FMT>), dim3((unsigned)pl.wgs), dim3(kGemvThreads), lds, stream,
-                       a);
+                       w[0], w[1], w[2], w[3], w[4], w[5], w[6], ka.slots, a);
   return hipGetLastError();
 }
 }  // namespace

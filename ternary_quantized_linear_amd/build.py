@@ -34,9 +34,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-source additions: the decode GEMV takes its leading scalar arguments (8 dwords)
-# preloaded into SGPRs at wave launch.
-EXTRA = {"bl_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
+# Per-source additions: the decode GEMV and the skinny product take their leading scalar
+# arguments (8 dwords) preloaded into SGPRs at wave launch.
+PRELOAD8 = ["-mllvm", "-amdgpu-kernarg-preload-count=8"]
+EXTRA = {"bl_gemv.hip": PRELOAD8, "bl_skinny.hip": PRELOAD8}
 
 
 def _compile(src):

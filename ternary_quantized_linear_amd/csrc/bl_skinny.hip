@@ -46,6 +46,7 @@
 #include "bl_plan.h"
 
 #include <climits>
+#include <cstddef>
 
 namespace bl {
 
@@ -87,6 +88,19 @@ struct SkArgs {
 };
 
 typedef const SkArgs __attribute__((address_space(4)))* SkArgsPtr;
+
+// The kernel's argument list: the starts of entries 1..7 and the regroup offset come
+// first, as scalars, so that they can be preloaded into SGPRs at wave launch (the build
+// asks for 8 preloaded dwords): a wave of a launch with up to 8 entries finds its entry
+// without a round trip to the argument memory, and the entry's fields are its first
+// load. Launches with more entries read the remaining starts from SkArgs.
+struct SkKernArgs {
+  int wg0[7];  // first workgroup of entries 1..7 (INT_MAX when unused)
+  int wbase;
+  SkArgs s;
+};
+constexpr int kSkArgsOffset = 32;
+static_assert(offsetof(SkKernArgs, s) == kSkArgsOffset, "argument layout");
 
 __device__ __forceinline__ SkProj load_sk(SkArgsPtr a, int i) {
   SkProj P;
@@ -382,13 +396,18 @@ __device__ __forceinline__ void sk_sweep(const SkProj& P, int T, int wgl, int wa
 }
 
 template <int TB>
-__global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
+__global__ __launch_bounds__(kSkThreads) void skinny_kernel(int w1, int w2, int w3, int w4, int w5,
+                                                             int w6, int w7, int wbase, SkArgs) {
   extern __shared__ int sk_lds[];
-  const SkArgsPtr a = (SkArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  const SkArgsPtr a = (SkArgsPtr)((const char __attribute__((address_space(4)))*)
+                                      __builtin_amdgcn_kernarg_segment_ptr() + kSkArgsOffset);
   const int wg = (int)blockIdx.x;
-  int pi = 0;
+  // the starts ascend, unused ones are INT_MAX: the entry is the count of starts <= wg
+  int pi = (wg >= w1) + (wg >= w2) + (wg >= w3) + (wg >= w4) + (wg >= w5) + (wg >= w6) + (wg >= w7);
+  if (pi == 7) {
 #pragma unroll
-  for (int i = 1; i < plan::kSkEntries; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
+    for (int i = 8; i < plan::kSkEntries; ++i) pi += wg >= a->wg0[i] ? 1 : 0;
+  }
   const SkProj P = load_sk(a, pi);
   const int T = P.T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kernel(SkArgs) {
   // Every wave passes exactly one barrier: in its sweep (in the set-up, or in the first
   // step with one token block: a working wave has at least one step), or here (leftover
   // waves without a segment, and segment lengths no plan gives).
-  uint8_t* const wlds = reinterpret_cast<uint8_t*>(sk_lds) + a->wbase;
+  uint8_t* const wlds = reinterpret_cast<uint8_t*>(sk_lds) + wbase;
   bool swept = false;
   if (wave < P.S * P.teams) {
     swept = true;
@@ -477,7 +496,9 @@ hipError_t launch_skinny_t(const bl_proj_internal* p, int count, const int* T, h
   a.wbase = pl.wbase;
   const int wgs = pl.wgs;
   const size_t lds = pl.lds;
-  hipLaunchKernelGGL(skinny_kernel<TB>, dim3((unsigned)wgs), dim3(kSkThreads), lds, stream, a);
+  const int* w = a.wg0;
+  hipLaunchKernelGGL(skinny_kernel<TB>, dim3((unsigned)wgs), dim3(kSkThreads), lds, stream, w[1], w[2],
+                     w[3], w[4], w[5], w[6], w[7], a.wbase, a);
   return hipGetLastError();
 }
 

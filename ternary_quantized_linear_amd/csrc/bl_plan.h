@@ -164,9 +164,14 @@ struct SkPlan {
 
 // Segment length and team shape for K: the largest fraction of wave-steps spent on real
 // codes (segments past K, idle waves and passes that leave waves without a segment
-// count as waste); ties go to the longer segment. TB: token blocks of 16 (1, 2 or 4);
-// a wave holds 16 * mpw * TB registers of activations, so more token blocks take
-// shorter segments (mpw <= 4 for two, <= 2 for four).
+// count as waste); ties go to the longer segment, except that with one token block,
+// rows needing several passes at 7 x 256 codes take segments of 512 codes when those
+// waste no more (70B down, K = 28672, at 8 / 12 / 15 tokens: 19.2 / 19.9 / 21.4 us
+// against 20.0 / 22.3 / 23.8 us in two passes of 7 x 256, the same at 2-4 tokens;
+// segments of 256 codes were slower).
+// TB: token blocks of 16 (1, 2 or 4); a wave holds 16 * mpw * TB registers of
+// activations, so more token blocks take shorter segments (mpw <= 4 for two, <= 2 for
+// four).
 inline void sk_segments(int K, int TB, SkEntry& s) {
   const int c = K / 256;
   const int cand[4] = {7, 4, 2, 1};
@@ -178,7 +183,8 @@ inline void sk_segments(int K, int TB, SkEntry& s) {
     const int teams = kSkWaves / S;
     const int npass = (nseg + S - 1) / S;
     const double e = (double)teams * c / ((double)kSkWaves * m * npass);
-    if (e > best + 1e-9) {
+    const bool multi = m == 2 && TB == 1 && s.mpw == 7 && s.npass > 1 && e > best - 1e-9;
+    if (e > best + 1e-9 || multi) {
       best = e;
       s.mpw = m;
       s.nseg = nseg;

@@ -80,13 +80,13 @@ bl_kernel choose(int64_t T, int64_t N, int64_t K, size_t ws_bytes = 0) {
   // one token: dot4 GEMV. Up to 128 tokens the streaming MFMA kernel (passes of 64),
   // except where the LDS-tiled GEMM measures faster: from 96 tokens on, beyond 64 (a
   // second streaming pass) when it can cut K into slices that fill the device (which
-  // takes a workspace for the partials), from 16 when it can and K >= 16384 (the
-  // streaming kernel reloads its activations many times over long rows), or when its
-  // 128 x 128 tiles alone give every CU two workgroups. Beyond 128 tokens the tiled
-  // GEMM. Measured on the 70B shapes: gate (K = 8192) at 32 / 48 / 64 / 80 tokens
-  // 21 / 30 / 33 / 49 us streaming against 27 / 34 / 37 / 44 us split; down
-  // (K = 28672) at 8 / 12 / 16 / 32 tokens 19.8 / 22.1 / 24.6 / 37 us streaming against
-  // 23.1 / 23.3 / 23.5 / 25.1 us split.
+  // takes a workspace for the partials), beyond 16 (two token blocks) when it can and
+  // K >= 16384 (the streaming kernel reloads its activations many times over long
+  // rows), or when its 128 x 128 tiles alone give every CU two workgroups. Beyond 128
+  // tokens the tiled GEMM. Measured on the 70B shapes: gate (K = 8192) at 32 / 48 / 64 /
+  // 80 tokens 21 / 30 / 33 / 49 us streaming against 27 / 34 / 37 / 44 us split; down
+  // (K = 28672, 512-code segments) at 12 / 14 / 16 / 17 / 32 tokens 20.8 / 20.8 / 22.3 /
+  // 26.9 / 37 us streaming against 23.6 / 23.4 / 23.6 / 24.0 / 25.1 us split.
   if (bl_gemv_supports((int)T, (int)K)) return BL_KERNEL_GEMV;
   const bool tiled = bl_prefill_supports((int)T, (int)K);
   if (bl_skinny_supports((int)T, N, (int)K)) {
@@ -94,7 +94,7 @@ bl_kernel choose(int64_t T, int64_t N, int64_t K, size_t ws_bytes = 0) {
     const bool split = tiled && bl_prefill_splits((int)T, (int)N, (int)K) &&
                        ws_bytes >= bl_prefill_scratch_bytes((int)T, (int)N, (int)K);
     const bool prefer_tiled = tiled && (T >= 96 || (T > 64 && split) ||
-                                        (T >= 16 && K >= 16384 && split) ||
+                                        (T > 16 && K >= 16384 && split) ||
                                         (T > 32 && tiles >= 512));
     if (!prefer_tiled) return BL_KERNEL_SKINNY;
   }

@@ -229,10 +229,10 @@ def test_split_k_workspace_query_and_validation(lib):
     c = lib.bitlinear_forward_choice_ws
     c.argtypes = [I64, I64, I64, ctypes.c_size_t]
     c.restype = ctypes.c_int
-    for T, N, K, k in [(15, 8192, 28672, 2), (16, 8192, 28672, 3), (64, 8192, 28672, 3),
+    for T, N, K, k in [(16, 8192, 28672, 2), (17, 8192, 28672, 3), (64, 8192, 28672, 3),
                        (32, 28672, 8192, 2), (64, 28672, 8192, 2), (65, 28672, 8192, 3),
                        (64, 4096, 4096, 2)]:
-        # from 16 tokens at K >= 16384, beyond 64 (a second streaming pass) when the
+        # beyond 16 tokens at K >= 16384, beyond 64 (a second streaming pass) when the
         # slices fill the device (112 row tiles x 3 slices, 32 x 8); 16 row tiles x 4
         # slices do not
         assert c(T, N, K, q(T, N, K)) == k, (T, N, K)

@@ -672,9 +672,12 @@ hipError_t bl_launch_prefill(const bl_proj_internal* p, int T, int32_t* scratch,
     }
   }
   const int64_t tiles = (int64_t)((T + 127) / 128) * ((p->N + 255) / 256);
+  // (one per CU: a third register set in the ring, which the AGPRs leave room for; the
+  // 2048 x 4096 x 14336 product 127.2 / 127.5 -> 123.7 / 124.3 us in alternating runs,
+  // four sets 125.1 / 126.1)
   if (T >= 128 && tiles >= cus)
     return tiles > cus ? launch_prefill_big<4, 2, 1, 2, 2>(p, T, 1, nullptr, stream)
-                       : launch_prefill_big<4, 2, 1, 1, 2>(p, T, 1, nullptr, stream);
+                       : launch_prefill_big<4, 2, 1, 1, 3>(p, T, 1, nullptr, stream);
   const int64_t big = (int64_t)((T + 255) / 256) * ((p->N + 127) / 128);
   if (T >= 256 && big >= 512) return launch_prefill_t<256, 128>(p, T, stream);
   return launch_prefill_t<128, 128>(p, T, stream);

@@ -268,8 +268,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PfArgs a) {
 //     set is refilled at once with k-tile kt + 1 + RD, in three parts spread over the
 //     MFMA steps; one barrier per k-tile. A load so has RD k-tiles to arrive (a second
 //     set that is loaded while the first is staged would give it one): the big tiles
-//     take RD = 2, the few-token tiles, with one workgroup per CU and little work per
-//     k-tile, a deeper ring.
+//     take RD = 2 at two workgroups per CU and 3 at one, the few-token tiles, with one
+//     workgroup per CU and little work per k-tile, a deeper ring.
 //   - Split K (a.P > 1): workgroup tile and slice come from one index (the tiles of a
 //     slice adjacent, so an XCD's workgroups share activation k-tiles); the slice's
 //     exact partial (token sums already subtracted) goes to plane p of a.part, and

@@ -282,24 +282,6 @@ def run_decode(torch, bl, d, steps, warmup):
     g_a = _warm_then_capture(torch, [qa] * 128)
     g_a.replay()
     ms_act = _time_graph(torch, g_a, 2) / 128
-    # each projection alone, rotating over the replicas (k, v and q, o are too small to
-    # stream at full rate: their time is mostly the launch)
-    per_proj = {}
-    names = [(p, inp) for _, parts, inp in FUSED for p in parts]
-    for j, (p, inp) in enumerate(names):
-        Xq, xs = d["acts"][inp]
-        T = Xq.shape[0]
-        v0 = d["layer_views"][0][j]
-        N, K = v0.shape[0], v0.shape[1] * 4
-        Y = torch.empty((T, N), dtype=torch.float32, device=Xq.device)
-        fp = [bl.prepare_forward_grouped([(Xq, xs, views[j], d["betas"][p], Y, None)], T)
-              for views in d["layer_views"]]
-        g_p = _warm_then_capture(torch, [fp[i % len(fp)] for i in range(n_k)])
-        g_p.replay()
-        ms_p = _time_graph(torch, g_p, 2) / n_k
-        gbs = gemv_bytes(T, N, K) / (ms_p * 1e-3) / 1e9
-        per_proj[p] = {"N": N, "K": K, "us": round(ms_p * 1e3, 3), "gbs": round(gbs, 1),
-                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     # the read roof of the same bytes: one read of a replica's allocation, and of the
     # seven projection views of it, rotating over the replicas like the products
     # (each of the four block schedules of the read kernel; the fastest is the roof)
@@ -326,9 +308,32 @@ def run_decode(torch, bl, d, steps, warmup):
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / 64
     return {"ms_step": ms_step, "ms_gemv": ms_gemv, "ms_act": ms_act, "ms_eager": ms_eager,
-            "ms_gemv7": ms_gemv7, "ms_read": ms_read, "ms_read7": ms_read7, "per_proj": per_proj,
+            "ms_gemv7": ms_gemv7, "ms_read": ms_read, "ms_read7": ms_read7,
             "step_stats": step_stats, "gemv_stats": _stats_us(gemv_samples),
             "clocks_before": clk0, "clocks_after": clk1}
+
+
+def run_decode_per_projection(torch, bl, d, n_k=256):
+    """Each decode8b projection launched alone (n_k graph-replayed launches rotating over
+    the replicas): us, GB/s and % of HBM. k, v and q, o are too small to stream at full
+    rate: their time is mostly the launch."""
+    per_proj = {}
+    names = [(p, inp) for _, parts, inp in FUSED for p in parts]
+    for j, (p, inp) in enumerate(names):
+        Xq, xs = d["acts"][inp]
+        T = Xq.shape[0]
+        v0 = d["layer_views"][0][j]
+        N, K = v0.shape[0], v0.shape[1] * 4
+        Y = torch.empty((T, N), dtype=torch.float32, device=Xq.device)
+        fp = [bl.prepare_forward_grouped([(Xq, xs, views[j], d["betas"][p], Y, None)], T)
+              for views in d["layer_views"]]
+        g_p = _warm_then_capture(torch, [fp[i % len(fp)] for i in range(n_k)])
+        g_p.replay()
+        ms_p = _time_graph(torch, g_p, 2) / n_k
+        gbs = gemv_bytes(T, N, K) / (ms_p * 1e-3) / 1e9
+        per_proj[p] = {"N": N, "K": K, "us": round(ms_p * 1e3, 3), "gbs": round(gbs, 1),
+                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return per_proj
 
 
 def run_mfma_roof(torch, bl, iters=2000):
@@ -958,12 +963,13 @@ def main():
                                    "of its four block schedules)"},
                      "seven_buffer_launch_us": round(r["ms_gemv7"] * 1e3, 3),
                      "packed_weight_gbs": round(d["packed_bytes"] / (r["ms_gemv"] * 1e-3) / 1e9, 1)},
-        "decode8b_per_projection": r["per_proj"],
         "act_quant": {"avg_launch_us": round(r["ms_act"] * 1e3, 3),
                       "bytes_per_launch": d["act_bytes"]},
         "clocks": {"before": r["clocks_before"], "after": r["clocks_after"]},
         "eager_ms_per_step": round(r["ms_eager"], 4),
     }
+    if not a.only_decode:
+        line["decode8b_per_projection"] = run_decode_per_projection(torch, bl, d)
     del d["bufs"], d["layer_views"], d["fws"], d["fws7"]
     torch.cuda.empty_cache()
     line["mfma_roof"] = run_mfma_roof(torch, bl)
